@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Throughput of exact causal sliding-window attention (+ sinks) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Prints ONE JSON line.  The default workload is the Mistral-7B-shaped prefill
+(batch 1, 32 heads, n=16384, d=128, w=4096, bf16): one step = one prefill
+launch over the whole prompt, inputs already resident in HBM.  `value` is
+band-TFLOP/s: 4*d FLOP per attended (query, key) pair (two products, a
+multiply-add counted as 2), attended pairs counted exactly per row.  The
+same line carries the rolling-cache decode workload (batch 64, 32 heads,
+d=128, w=4096, g=4, positions in [4096, 131072]) as KV GB/s: bytes of the
+key/value rows each query attends, plus q and o.
+
+`roofline` is for the dominant kernel of the line's workload, timed with
+events on the stream the kernel runs on.  `cpu_baseline` is the fp64 oracle
+on a bounded sample of the same workload, on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SWA prefill band-TFLOP/s and decode KV GB/s, % of MI355X peak, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (matrix and vector)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+PREFILL = {
+    # name: (batch, heads, n, d, w, g, sink_bias, seed)
+    "tiny_fp32": (1, 1, 256, 64, 64, 0, 0.0, 1),
+    "mistral_prefill": (1, 32, 16384, 128, 4096, 0, 0.0, 2),
+    "sink_prefill": (1, 32, 32768, 128, 4096, 4, 4.0, 3),
+    "gemma3_local_prefill": (1, 16, 131072, 128, 1024, 0, 0.0, 5),
+}
+DECODE = {
+    # name: (batch, heads, d, w, g, pos_lo, pos_hi, seed)
+    "rolling_decode": (64, 32, 128, 4096, 4, 4096, 131072, 4),
+}
+
+# Traffic measured with rocprofv3 counters (FETCH_SIZE + WRITE_SIZE per
+# dispatch, scaled by the copy-kernel calibration); None until measured for
+# the kernel as it stands.
+MEASURED_TRAFFIC_BYTES = {}
+
+
+def row_pairs(i: int, w: int, g: int) -> int:
+    """|A_i|: window keys min(i+1, w) plus sink keys below the window."""
+    return min(i + 1, w) + min(g, max(0, i - w + 1))
+
+
+def band_pairs(n: int, w: int, g: int) -> int:
+    # closed form of sum_i row_pairs(i, w, g)
+    m = min(n, w)
+    pairs = m * (m + 1) // 2 + (n - m) * w
+    if g > 0 and n > w:
+        # rows i >= w see min(g, i-w+1) sinks below the window
+        k = n - w  # number of rows with i - w + 1 >= 1
+        full = max(0, k - g)  # rows seeing all g sinks
+        ramp = k - full       # rows seeing 1..ramp sinks
+        pairs += ramp * (ramp + 1) // 2 + full * g
+    return pairs
+
+
+def _events_time(fn, steps, stream):
+    import torch
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in evs]
+    total = t0.elapsed_time(t1)
+    return total / steps, sum(per) / len(per), per
+
+
+def bench_prefill(name, steps, warmup):
+    import torch
+
+    import block_sparse_causal_band_amd as swa
+    from block_sparse_causal_band_amd import synth
+
+    B, H, n, d, w, g, beta, seed = PREFILL[name]
+    dtype = torch.float32 if name == "tiny_fp32" else torch.bfloat16
+    dev = torch.device("cuda")
+    q, k, v = synth.qkv(B, H, n, d, dtype, seed=seed, device=dev)
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        swa.prefill(q, k, v, w=w, g=g, sink_bias=beta, out=o)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ms_step, ms_launch, per = _events_time(step, steps, stream)
+    flops = 4.0 * d * band_pairs(n, w, g) * B * H
+    peak = PEAK_BF16_TFLOPS if dtype == torch.bfloat16 else PEAK_F32_TFLOPS
+    achieved = flops / (ms_launch * 1e-3) / 1e12
+    traffic = MEASURED_TRAFFIC_BYTES.get(name)
+    return {
+        "ms_per_step": ms_step,
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "dtype": "bf16" if dtype == torch.bfloat16 else "f32",
+        "config": {"workload": name, "batch": B, "heads": H, "n": n, "d": d, "w": w, "g": g,
+                   "sink_bias": beta, "band_flops_per_step": flops,
+                   "page_formula_flops_4nwd": 4.0 * n * w * d * B * H},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic,
+                     "kernel": f"prefill_kernel<{'bf16' if dtype == torch.bfloat16 else 'f32'},{d}>",
+                     "avg_launch_ms": ms_launch, "min_launch_ms": min(per)},
+    }
+
+
+def bench_decode(name, steps, warmup):
+    import torch
+
+    import block_sparse_causal_band_amd as swa
+    from block_sparse_causal_band_amd import synth
+
+    B, H, d, w, g, lo, hi, seed = DECODE[name]
+    dev = torch.device("cuda")
+    q, kc, vc, pos = synth.decode_problem(B, H, d, g + w, lo, hi, torch.bfloat16, seed=seed, device=dev)
+    o = torch.empty_like(q)
+    ws_bytes = swa.decode_workspace_bytes(B, H, d, w, g)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        swa.decode(q, kc, vc, pos, w=w, g=g, out=o, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ms_step, ms_launch, per = _events_time(step, steps, stream)
+    # algorithmic bytes: each query's attended K and V rows once, plus q and o
+    rows = sum(row_pairs(int(p), w, g) for p in pos.cpu().tolist()) * H
+    nbytes = rows * d * 2 * 2 + 2 * B * H * d * 2
+    achieved = nbytes / (ms_launch * 1e-3) / 1e9
+    traffic = MEASURED_TRAFFIC_BYTES.get(name)
+    return {
+        "ms_per_step": ms_step,
+        "value": nbytes / (ms_step * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "dtype": "bf16",
+        "config": {"workload": name, "batch": B, "heads": H, "d": d, "w": w, "g": g,
+                   "positions": [lo, hi], "kv_bytes_per_step": nbytes},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic, "kernel": "decode_kernel<bf16,128>",
+                     "avg_launch_ms": ms_launch, "min_launch_ms": min(per)},
+    }
+
+
+def cpu_baseline_prefill(name, budget_s=12.0):
+    """The fp64 oracle, as it stands, on whole heads of the same workload until
+    about budget_s seconds of CPU work; rate in band-TFLOP/s."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from block_sparse_causal_band_amd import synth
+
+    B, H, n, d, w, g, beta, seed = PREFILL[name]
+    dtype = torch.float32 if name == "tiny_fp32" else torch.bfloat16
+    q, k, v = synth.qkv(B, H, n, d, dtype, seed=seed, device="cpu")
+    orc = oracle.default()
+    rows_per_chunk = 512 if n >= 4096 else n
+    done_pairs = 0
+    done_rows = 0
+    heads_touched = 0
+    t0 = time.perf_counter()
+    # whole heads, each from its last rows backwards (full-window rows are the
+    # bulk of the workload), until the budget is spent
+    for bh in range(B * H):
+        if time.perf_counter() - t0 >= budget_s:
+            break
+        b, h = divmod(bh, H)
+        heads_touched += 1
+        start = n - rows_per_chunk
+        while time.perf_counter() - t0 < budget_s and start > -rows_per_chunk:
+            rows = np.arange(max(0, start), start + rows_per_chunk)
+            orc.prefill(q[b, h], k[b, h], v[b, h], w=w, g=g, beta=beta, rows=rows)
+            done_pairs += sum(row_pairs(int(i), w, g) for i in rows)
+            done_rows += len(rows)
+            start -= rows_per_chunk
+    dt = time.perf_counter() - t0
+    return {
+        "value": 4.0 * d * done_pairs / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": orc.num_threads(),
+        "kind": "oracle",
+        "sample": f"{done_rows} query rows over {heads_touched} head(s) of {name} (each head from its "
+                  f"last row backwards), fp64, {dt:.1f} s",
+    }
+
+
+def cpu_baseline_decode(name, budget_s=10.0):
+    import numpy as np
+    import torch
+
+    import oracle
+    from block_sparse_causal_band_amd import synth
+
+    B, H, d, w, g, lo, hi, seed = DECODE[name]
+    orc = oracle.default()
+    rng = np.random.default_rng(seed)
+    nk = g + w
+    units = 64
+    q = synth.normal((units, d), seed=seed, dtype=torch.bfloat16)
+    kk = synth.normal((units, nk, d), seed=seed + 2, dtype=torch.bfloat16)
+    vv = synth.normal((units, nk, d), seed=seed + 3, dtype=torch.bfloat16)
+    done_bytes = 0
+    done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        ps = rng.integers(lo, hi + 1, units)
+        kpos = np.stack([np.concatenate([np.arange(p - w + 1, p + 1), np.arange(0, min(g, p - w + 1))])
+                         for p in ps])
+        orc.decode(q, ps, kpos, kk, vv, w=w, g=g)
+        done_bytes += sum(row_pairs(int(p), w, g) for p in ps) * d * 2 * 2 + 2 * units * d * 2
+        done += units
+    dt = time.perf_counter() - t0
+    return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"{done} (batch, head) queries of {name}, fp64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mistral_prefill", choices=sorted(PREFILL) + sorted(DECODE))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode figures on a prefill line")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(heads and batch shard with no exchange; see the design notes). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+
+    if args.workload in PREFILL:
+        r = bench_prefill(args.workload, args.steps, args.warmup)
+    else:
+        r = bench_decode(args.workload, args.steps, args.warmup)
+    line = {
+        "metric": METRIC,
+        "value": r["value"],
+        "unit": r["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": r["dtype"],
+        "data": "synthetic: iid N(0,1) inputs from seeded torch generators, rounded to the dtype",
+        "config": r["config"],
+        "roofline": r["roofline"],
+    }
+    line["roofline"]["frac_str"] = f"{100 * r['roofline']['frac']:.1f}% of MI355X peak"
+    if args.workload in PREFILL and not args.no_decode:
+        dname = "rolling_decode"
+        dr = bench_decode(dname, args.steps, args.warmup)
+        line["decode"] = {"value": dr["value"], "unit": dr["unit"], "ms_per_step": dr["ms_per_step"],
+                          "config": dr["config"], "roofline": dr["roofline"]}
+    if not args.no_cpu_baseline:
+        if args.workload in PREFILL:
+            line["cpu_baseline"] = cpu_baseline_prefill(args.workload)
+        else:
+            line["cpu_baseline"] = cpu_baseline_decode(args.workload)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

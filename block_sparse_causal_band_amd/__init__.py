@@ -1,0 +1,24 @@
+"""Exact causal sliding-window attention with attention sinks for AMD MI355X.
+
+The computation lives in libswa.so (hand-written HIP kernels for gfx950
+behind the C ABI of include/swa.h); this package is its thin Python binding.
+
+    from block_sparse_causal_band_amd import prefill, kv_append, decode
+
+Importing the package does not load the library; the first call does, and
+raises if it is not built (``python -m block_sparse_causal_band_amd.build``).
+"""
+from .binding import (  # noqa: F401
+    SWA_BF16,
+    SWA_F32,
+    SwaError,
+    band_tiles,
+    decode,
+    decode_workspace_bytes,
+    kv_append,
+    lib,
+    prefill,
+    prefill_order,
+    prefill_tile_shape,
+    strerror,
+)

@@ -1,0 +1,210 @@
+"""Python binding of libswa.so (include/swa.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  Tensors are torch tensors on a ROCm device; the
+binding checks their shapes, dtypes and layout, passes raw device pointers,
+and enqueues on torch's current stream of the tensors' device.  There is no
+fallback: if libswa.so is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libswa.so")
+
+SWA_F32 = 0
+SWA_BF16 = 1
+
+_vp = ctypes.c_void_p
+_int = ctypes.c_int
+_flt = ctypes.c_float
+
+
+class SwaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: status {status} ({strerror(status)})")
+        self.status = status
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libswa.so (built in-tree by ``python -m block_sparse_causal_band_amd.build``)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built: run `python -m block_sparse_causal_band_amd.build` "
+                "(there is no fallback implementation)"
+            )
+        L = ctypes.CDLL(LIB_PATH)
+        L.swa_prefill_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _int,
+                                      _flt, _flt, _int, _vp]
+        L.swa_prefill_fwd.restype = _int
+        L.swa_kv_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _int, _int, _vp]
+        L.swa_kv_append.restype = _int
+        L.swa_decode_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int,
+                                     _flt, _flt, _int, _vp, ctypes.c_size_t, _vp]
+        L.swa_decode_fwd.restype = _int
+        L.swa_decode_workspace_bytes.argtypes = [_int] * 5
+        L.swa_decode_workspace_bytes.restype = ctypes.c_size_t
+        L.swa_strerror.argtypes = [_int]
+        L.swa_strerror.restype = ctypes.c_char_p
+        L.swa_band_tiles.argtypes = [_int, _int, _int, _int, _int, _vp, ctypes.c_long]
+        L.swa_band_tiles.restype = ctypes.c_long
+        L.swa_prefill_tile_shape.argtypes = [_int, _int, ctypes.POINTER(_int), ctypes.POINTER(_int)]
+        L.swa_prefill_tile_shape.restype = _int
+        L.swa_prefill_order.argtypes = [_int, _int, _vp, ctypes.c_long]
+        L.swa_prefill_order.restype = ctypes.c_long
+        _LIB = L
+    return _LIB
+
+
+def strerror(status: int) -> str:
+    return lib().swa_strerror(int(status)).decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return SWA_BF16
+    if t.dtype == torch.float32:
+        return SWA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _stream(t) -> int:
+    import torch
+
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev_tensor(t, name):
+    import torch
+
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch tensor")
+    _need(t.is_cuda, f"{name} must be on a ROCm device")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def prefill(q, k, v, w: int, g: int = 0, scale: float | None = None, sink_bias: float = 0.0,
+            return_lse: bool = False, out=None):
+    """Causal sliding-window attention with sinks over q, k, v [batch, heads, n, d]."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(t, name)
+    _need(q.dim() == 4 and q.shape == k.shape == v.shape, "q, k, v must share one shape [batch, heads, n, d]")
+    _need(q.dtype == k.dtype == v.dtype, "q, k, v must share one dtype")
+    _need(q.device == k.device == v.device, "q, k, v must be on one device")
+    B, H, n, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    _dev_tensor(o, "out")
+    _need(o.shape == q.shape and o.dtype == q.dtype and o.device == q.device, "out must match q")
+    lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device) if return_lse else None
+    rc = lib().swa_prefill_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                               lse.data_ptr() if lse is not None else None,
+                               B, H, n, d, int(w), int(g), float(scale), float(sink_bias),
+                               _dtype_code(q), _stream(q))
+    if rc != 0:
+        raise SwaError(rc, "swa_prefill_fwd")
+    return (o, lse) if return_lse else o
+
+
+def kv_append(k_cache, v_cache, k_new, v_new, pos, w: int, g: int = 0):
+    """Write k_new, v_new [batch, heads, t, d] at positions pos[b] .. pos[b]+t-1."""
+    import torch
+
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("k_new", k_new), ("v_new", v_new), ("pos", pos)):
+        _dev_tensor(t, name)
+    B, H, R, d = k_cache.shape
+    _need(v_cache.shape == k_cache.shape, "k_cache and v_cache must share one shape")
+    _need(R == g + w, f"cache must hold g + w = {g + w} rows per (batch, head)")
+    _need(k_new.dim() == 4 and k_new.shape[:2] == (B, H) and k_new.shape[3] == d, "k_new must be [batch, heads, t, d]")
+    _need(v_new.shape == k_new.shape, "v_new must match k_new")
+    _need(len({k_cache.dtype, v_cache.dtype, k_new.dtype, v_new.dtype}) == 1, "one dtype for cache and new tokens")
+    _need(pos.dtype == torch.int64 and pos.shape == (B,), "pos must be int64 [batch]")
+    rc = lib().swa_kv_append(k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                             pos.data_ptr(), B, H, k_new.shape[2], d, int(w), int(g),
+                             _dtype_code(k_cache), _stream(k_cache))
+    if rc != 0:
+        raise SwaError(rc, "swa_kv_append")
+
+
+def decode_workspace_bytes(batch: int, heads: int, d: int, w: int, g: int) -> int:
+    return int(lib().swa_decode_workspace_bytes(batch, heads, d, w, g))
+
+
+def decode(q, k_cache, v_cache, pos, w: int, g: int = 0, scale: float | None = None, sink_bias: float = 0.0,
+           return_lse: bool = False, workspace=None, out=None):
+    """One query per (batch, head), q [batch, heads, d], at positions pos [batch]."""
+    import torch
+
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("pos", pos)):
+        _dev_tensor(t, name)
+    B, H, d = q.shape
+    _need(k_cache.shape == v_cache.shape == (B, H, g + w, d), f"caches must be [batch, heads, g + w, d]")
+    _need(q.dtype == k_cache.dtype == v_cache.dtype, "one dtype for q and the caches")
+    _need(pos.dtype == torch.int64 and pos.shape == (B,), "pos must be int64 [batch]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    _dev_tensor(o, "out")
+    _need(o.shape == q.shape and o.dtype == q.dtype, "out must match q")
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if return_lse else None
+    need = decode_workspace_bytes(B, H, d, w, g)
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().swa_decode_fwd(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), pos.data_ptr(), o.data_ptr(),
+                              lse.data_ptr() if lse is not None else None, B, H, d, int(w), int(g),
+                              float(scale), float(sink_bias), _dtype_code(q), ws_ptr, ws_bytes, _stream(q))
+    if rc != 0:
+        raise SwaError(rc, "swa_decode_fwd")
+    return (o, lse) if return_lse else o
+
+
+def band_tiles(n: int, w: int, g: int, bq: int, bk: int) -> np.ndarray:
+    """The prefill tile schedule as an int array [tiles, 3] = (query block, key block, is_full)."""
+    L = lib()
+    count = L.swa_band_tiles(n, w, g, bq, bk, None, 0)
+    if count < 0:
+        raise SwaError(count, "swa_band_tiles")
+    out = np.zeros((max(count, 1), 3), dtype=np.int32)
+    got = L.swa_band_tiles(n, w, g, bq, bk, out.ctypes.data, count)
+    if got != count:
+        raise SwaError(got, "swa_band_tiles")
+    return out[:count]
+
+
+def prefill_tile_shape(dtype_code: int, d: int):
+    bq, bk = _int(), _int()
+    rc = lib().swa_prefill_tile_shape(dtype_code, d, ctypes.byref(bq), ctypes.byref(bk))
+    if rc != 0:
+        raise SwaError(rc, "swa_prefill_tile_shape")
+    return bq.value, bk.value
+
+
+def prefill_order(units: int, nqb: int) -> np.ndarray:
+    """Workgroup id -> (unit, query block) of a prefill launch, as int array [units*nqb, 2]."""
+    total = units * nqb
+    out = np.zeros((total, 2), dtype=np.int32)
+    got = lib().swa_prefill_order(units, nqb, out.ctypes.data, total)
+    if got != total:
+        raise SwaError(got, "swa_prefill_order")
+    return out

@@ -1,0 +1,162 @@
+// api.cpp -- the C ABI of libswa.so (declared in include/swa.h): argument
+// validation, dispatch to the HIP launchers, status codes, test hooks.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/swa.h"
+#include "schedule.h"
+
+namespace swa {
+hipError_t launch_prefill(const void *q, const void *k, const void *v, void *o, float *lse, int units, int n,
+                          int d, int w, int g, float scale, float sink_bias, bool bf16, hipStream_t stream);
+hipError_t launch_decode(const void *q, const void *kc, const void *vc, const int64_t *pos, void *o, float *lse,
+                         int units, int heads, int d, int w, int g, float scale, float sink_bias, bool bf16,
+                         void *ws, hipStream_t stream);
+hipError_t launch_kv_append(void *kc, void *vc, const void *kn, const void *vn, const int64_t *pos, int batch,
+                            int heads, int tn, int d, int w, int g, bool bf16, hipStream_t stream);
+size_t decode_workspace_bytes(int units, int d, int rows);
+// prefill tile shape (prefill.hip): 128 query rows x 64 keys for every dtype and d
+constexpr int kPrefillBQ = 128;
+constexpr int kPrefillBK = 64;
+}  // namespace swa
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int check_dtype_d(swa_dtype_t dtype, int d) {
+    if (dtype != SWA_F32 && dtype != SWA_BF16) return SWA_EUNSUPPORTED;
+    if (d != 64 && d != 128) return SWA_EUNSUPPORTED;
+    return SWA_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *swa_strerror(int status) {
+    switch (status) {
+        case SWA_OK: return "ok";
+        case SWA_EINVAL: return "invalid argument (size, count, scale or null pointer)";
+        case SWA_EUNSUPPORTED: return "unsupported head dimension or dtype (d must be 64 or 128; f32 or bf16)";
+        case SWA_EALIGN: return "pointer not aligned (tensors need 16 bytes, lse 4 bytes)";
+        case SWA_EHIP: return "the HIP runtime rejected a launch";
+        case SWA_EWORKSPACE: return "decode workspace missing or too small";
+        default: return "unknown status";
+    }
+}
+
+int swa_prefill_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int batch, int heads, int n,
+                    int d, int w, int g, float scale, float sink_bias, swa_dtype_t dtype, hipStream_t stream) {
+    if (!q || !k || !v || !o) return SWA_EINVAL;
+    if (batch < 1 || heads < 1 || n < 1 || w < 1 || g < 0) return SWA_EINVAL;
+    if (!std::isfinite(scale) || !(scale > 0.f) || !std::isfinite(sink_bias)) return SWA_EINVAL;
+    int st = check_dtype_d(dtype, d);
+    if (st != SWA_OK) return st;
+    if (n > INT_MAX - swa::kPrefillBQ) return SWA_EINVAL;
+    const long long units = (long long)batch * heads;
+    const long long nqb = (n + swa::kPrefillBQ - 1) / swa::kPrefillBQ;
+    if (units * nqb > INT_MAX) return SWA_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned4(lse)))
+        return SWA_EALIGN;
+    return status_of(swa::launch_prefill(q, k, v, o, lse, (int)units, n, d, w, g, scale, sink_bias,
+                                         dtype == SWA_BF16, stream));
+}
+
+int swa_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v_new, const int64_t *pos,
+                  int batch, int heads, int t_new, int d, int w, int g, swa_dtype_t dtype, hipStream_t stream) {
+    if (!k_cache || !v_cache || !k_new || !v_new || !pos) return SWA_EINVAL;
+    if (batch < 1 || heads < 1 || t_new < 0 || w < 1 || g < 0) return SWA_EINVAL;
+    if ((long long)g + w > INT_MAX) return SWA_EINVAL;
+    int st = check_dtype_d(dtype, d);
+    if (st != SWA_OK) return st;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new) ||
+        (reinterpret_cast<uintptr_t>(pos) & 7u))
+        return SWA_EALIGN;
+    if (t_new == 0) return SWA_OK;
+    const long long blocks = ((long long)batch * heads * t_new * (d * (dtype == SWA_BF16 ? 2 : 4) / 16) + 255) / 256;
+    if (blocks > INT_MAX) return SWA_EINVAL;
+    return status_of(swa::launch_kv_append(k_cache, v_cache, k_new, v_new, pos, batch, heads, t_new, d, w, g,
+                                           dtype == SWA_BF16, stream));
+}
+
+size_t swa_decode_workspace_bytes(int batch, int heads, int d, int w, int g) {
+    if (batch < 1 || heads < 1 || w < 1 || g < 0 || (d != 64 && d != 128)) return 0;
+    return swa::decode_workspace_bytes(batch * heads, d, g + w);
+}
+
+int swa_decode_fwd(const void *q, const void *k_cache, const void *v_cache, const int64_t *pos, void *o, float *lse,
+                   int batch, int heads, int d, int w, int g, float scale, float sink_bias, swa_dtype_t dtype,
+                   void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!q || !k_cache || !v_cache || !pos || !o) return SWA_EINVAL;
+    if (batch < 1 || heads < 1 || w < 1 || g < 0) return SWA_EINVAL;
+    if ((long long)g + w > INT_MAX / 2) return SWA_EINVAL;
+    if ((long long)batch * heads > INT_MAX / 64) return SWA_EINVAL;
+    if (!std::isfinite(scale) || !(scale > 0.f) || !std::isfinite(sink_bias)) return SWA_EINVAL;
+    int st = check_dtype_d(dtype, d);
+    if (st != SWA_OK) return st;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+        (reinterpret_cast<uintptr_t>(pos) & 7u) || (lse && !aligned4(lse)))
+        return SWA_EALIGN;
+    const size_t need = swa::decode_workspace_bytes(batch * heads, d, g + w);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return SWA_EWORKSPACE;
+        if (!aligned16(workspace)) return SWA_EALIGN;
+    }
+    return status_of(swa::launch_decode(q, k_cache, v_cache, pos, o, lse, batch * heads, heads, d, w, g, scale,
+                                        sink_bias, dtype == SWA_BF16, workspace, stream));
+}
+
+long swa_band_tiles(int n, int w, int g, int bq, int bk, int *out, long cap) {
+    if (n < 1 || w < 1 || g < 0 || bq < 1 || bk < 1 || cap < 0 || (cap > 0 && !out)) return SWA_EINVAL;
+    long count = 0;
+    const int nqb = (n + bq - 1) / bq;
+    for (int qb = 0; qb < nqb; ++qb) {
+        const int q0 = qb * bq;
+        const int q1 = (q0 + bq < n ? q0 + bq : n) - 1;
+        const swa::BandRange r = swa::band_range(q0, q1, w, g, bk);
+        for (int t = 0; t < r.count(); ++t) {
+            const int kb = r.block(t);
+            const int full = swa::tile_full(q0, q1, kb * bk, kb * bk + bk - 1, n, w, g) ? 1 : 0;
+            if (count < cap) {
+                out[3 * count + 0] = qb;
+                out[3 * count + 1] = kb;
+                out[3 * count + 2] = full;
+            }
+            ++count;
+        }
+    }
+    return count;
+}
+
+int swa_prefill_tile_shape(swa_dtype_t dtype, int d, int *bq, int *bk) {
+    int st = check_dtype_d(dtype, d);
+    if (st != SWA_OK) return st;
+    if (!bq || !bk) return SWA_EINVAL;
+    *bq = swa::kPrefillBQ;
+    *bk = swa::kPrefillBK;
+    return SWA_OK;
+}
+
+long swa_prefill_order(int units, int nqb, int *out, long cap) {
+    if (units < 1 || nqb < 1 || cap < 0 || (cap > 0 && !out)) return SWA_EINVAL;
+    const long long total = (long long)units * nqb;
+    if (total > INT_MAX) return SWA_EINVAL;
+    for (long long bid = 0; bid < total; ++bid) {
+        int u, qb;
+        swa::workgroup_order((int)bid, (int)total, nqb, &u, &qb);
+        if (bid < cap) {
+            out[2 * bid] = u;
+            out[2 * bid + 1] = qb;
+        }
+    }
+    return (long)total;
+}
+
+}  // extern "C"

@@ -1,0 +1,152 @@
+/*
+ * swa.h -- C ABI of libswa.so: exact causal sliding-window attention with
+ * attention sinks on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (from the pages this library implements):
+ *  - "Sliding Window and Sparse Attention, from Longformer to CSA2",
+ *    s1: Attention(Q, K, V) = softmax(Q K^T / sqrt(d)) V, causal (j <= i);
+ *    s2: sliding window -- query i reads keys i-w+1 .. i (w keys including
+ *        itself); attention sinks -- the first g tokens stay readable forever;
+ *        rolling-buffer cache -- position i overwrites slot i mod w;
+ *    s10 glossary, LSE: the log-sum-exp normaliser returned so that partial
+ *        results over disjoint key sets can be merged.
+ *  - "Local and Sparse Attention: Reading Fewer Token Positions", Figures 1,
+ *    2 and 4 and their text: a window of 3 counts the current token; an
+ *    excluded score is -inf before the softmax (never 0); a position that is
+ *    in the window and in the anchor (sink) set is read once; no future
+ *    position is read; a window-only cache overwrites the oldest slot.
+ *
+ * For query position i the attended key set is
+ *     A_i = { j : max(0, i-w+1) <= j <= i }  U  { j : 0 <= j < min(g, i+1) }
+ * and, with s_ij = scale * q_i . k_j + sink_bias * [j < g] for j in A_i,
+ *     o_i   = sum_{j in A_i} exp(s_ij - m_i) v_j / sum_{j in A_i} exp(s_ij - m_i),
+ *     lse_i = m_i + ln sum_{j in A_i} exp(s_ij - m_i),   m_i = max_j s_ij.
+ * sink_bias is an additive offset on the scaled score of every attended key
+ * at a position below g (0 gives plain sinks).
+ *
+ * Conventions for every entry point
+ *  - Tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates nothing and keeps no state between calls.  Every tensor is
+ *    contiguous with the innermost dimension last, as written below, and
+ *    every pointer must be 16-byte aligned.
+ *  - Work is enqueued asynchronously on `stream` (0 = the null stream); the
+ *    library never synchronises.  Device-side faults surface at the caller's
+ *    next synchronisation, as usual in HIP.
+ *  - Arguments are validated before anything is enqueued.  On an invalid
+ *    argument the call returns a negative status and launches nothing.
+ *    SWA_EHIP means a launch was rejected by the HIP runtime.
+ *  - Supported: dtype SWA_BF16 (bf16 storage, fp32 accumulation and softmax,
+ *    probabilities rounded to bf16 before the value product, bf16 output) and
+ *    SWA_F32 (fp32 throughout); head dimension d in {64, 128}.
+ *  - Calls on one stream are ordered; calls that write the same memory from
+ *    different streams race, as with any HIP kernel.
+ */
+#ifndef SWA_H
+#define SWA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype_t;
+
+enum {
+    SWA_OK = 0,
+    SWA_EINVAL = -1,        /* a size, a count or a required pointer is invalid */
+    SWA_EUNSUPPORTED = -2,  /* head dimension or dtype not supported            */
+    SWA_EALIGN = -3,        /* a pointer is not 16-byte aligned                 */
+    SWA_EHIP = -4,          /* the HIP runtime rejected a launch                */
+    SWA_EWORKSPACE = -5     /* decode workspace missing or too small            */
+};
+
+/*
+ * Prefill: attention of all n queries of each (batch, head) over the same
+ * sequence's keys, restricted to A_i.
+ *   q, k, v, o : [batch][heads][n][d]   (dtype)
+ *   lse        : [batch][heads][n] fp32, natural log; may be NULL
+ *   scale      : finite, > 0 (1/sqrt(d) is the usual value)
+ *   sink_bias  : finite
+ *   n >= 1, w >= 1, g >= 0 (g may exceed n), batch >= 1, heads >= 1,
+ *   batch * heads * n * d < 2^31.
+ * Only the key tiles that hold attended pairs are visited (the diagonal band
+ * plus the sink tiles below it); nothing n x n is ever formed.  K and V rows
+ * at positions >= n are never read.
+ */
+int swa_prefill_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                    int batch, int heads, int n, int d, int w, int g,
+                    float scale, float sink_bias, swa_dtype_t dtype, hipStream_t stream);
+
+/*
+ * Rolling-buffer cache append.  Cache layout, per (batch, head), g + w rows:
+ *   rows 0 .. g-1      : sinks, position t < g lives in row t (never overwritten)
+ *   rows g .. g+w-1    : ring, position t lives in row g + (t mod w)
+ *   k_cache, v_cache   : [batch][heads][g + w][d]   (dtype)
+ *   k_new, v_new       : [batch][heads][t_new][d]   (dtype)
+ *   pos                : [batch] int64, device; position of token 0 of each
+ *                        batch entry (token j is at pos[b] + j); must be >= 0
+ *                        (a negative entry makes that batch entry a no-op)
+ * A token at position P goes to ring row g + P mod w, and also to sink row P
+ * when P < g.  When t_new > w only the last w tokens reach the ring (the
+ * earlier ones would be overwritten anyway); sink rows are still written.
+ */
+int swa_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
+                  const int64_t *pos, int batch, int heads, int t_new, int d, int w, int g,
+                  swa_dtype_t dtype, hipStream_t stream);
+
+/*
+ * Decode: one query per (batch, head) at position pos[b] against the cache
+ * above.  Append-then-attend: the query's own key/value must already be in
+ * the cache, and every position 0 .. pos[b] must have been appended in order.
+ *   q, o      : [batch][heads][d]   (dtype)
+ *   lse       : [batch][heads] fp32 or NULL
+ *   pos       : [batch] int64, device, >= 0 (a negative entry yields NaN output)
+ *   workspace : device scratch of at least swa_decode_workspace_bytes(...)
+ *               bytes, 16-byte aligned, or NULL when that size is 0.
+ * Ring slot s is read only when it holds a position of the window; sink row t
+ * is read only when position t has left the window (otherwise the ring copy
+ * is the one read, so each position is read once).
+ */
+int swa_decode_fwd(const void *q, const void *k_cache, const void *v_cache, const int64_t *pos,
+                   void *o, float *lse, int batch, int heads, int d, int w, int g,
+                   float scale, float sink_bias, swa_dtype_t dtype,
+                   void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes swa_decode_fwd needs for this shape (0 when the launch
+ * does not split the cache rows of one (batch, head) across workgroups). */
+size_t swa_decode_workspace_bytes(int batch, int heads, int d, int w, int g);
+
+/* Static description of a status code. */
+const char *swa_strerror(int status);
+
+/*
+ * Test hook (host only, launches nothing): the prefill tile schedule.
+ * Writes triples (query_block, key_block, is_full) for every tile the
+ * prefill kernel visits when queries are grouped bq at a time and keys bk at
+ * a time, in visiting order, query block by query block.  is_full = 1 means
+ * every pair of the tile with query < n is attended and carries no sink bias,
+ * so the kernel skips masking there.  Returns the number of triples (writing
+ * at most `cap`), or a negative status.
+ */
+long swa_band_tiles(int n, int w, int g, int bq, int bk, int *out, long cap);
+
+/* Test hook: the tile shape the prefill kernel uses for (dtype, d). */
+int swa_prefill_tile_shape(swa_dtype_t dtype, int d, int *bq, int *bk);
+
+/*
+ * Test hook (host only): the workgroup -> (batch*head, query block) order of
+ * a prefill launch with `units` (batch, head) pairs and `nqb` query blocks.
+ * Writes pairs for workgroup ids 0 .. units*nqb-1.  Returns the count or a
+ * negative status.
+ */
+long swa_prefill_order(int units, int nqb, int *out, long cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWA_H */

@@ -1,0 +1,106 @@
+"""libswa.so loads, exports every entry point of include/swa.h, and rejects
+invalid arguments before launching anything.  CPU only: every call here
+fails validation, so no device work is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_causal_band_amd as swa
+from block_sparse_causal_band_amd import binding
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "swa.h")
+
+OK, EINVAL, EUNSUP, EALIGN, EHIP, EWS = 0, -1, -2, -3, -4, -5
+P = 4096  # a fake, 16-byte aligned "device pointer": never dereferenced on these paths
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(swa_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("swa_prefill_fwd", "swa_decode_fwd", "swa_kv_append", "swa_decode_workspace_bytes",
+                 "swa_strerror", "swa_band_tiles"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(binding.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), f"{name} not exported"
+
+
+def test_strerror_covers_every_status():
+    for st in (OK, EINVAL, EUNSUP, EALIGN, EHIP, EWS):
+        assert swa.strerror(st) and swa.strerror(st) != "unknown status"
+    assert swa.strerror(-99) == "unknown status"
+
+
+def _prefill(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, batch=1, heads=1, n=16, d=128, w=4, g=0,
+             scale=0.125, bias=0.0, dtype=1)
+    a.update(kw)
+    return swa.lib().swa_prefill_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["batch"], a["heads"], a["n"],
+                                     a["d"], a["w"], a["g"], a["scale"], a["bias"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), EINVAL), (dict(k=None), EINVAL), (dict(v=None), EINVAL), (dict(o=None), EINVAL),
+    (dict(batch=0), EINVAL), (dict(heads=0), EINVAL), (dict(n=0), EINVAL), (dict(w=0), EINVAL),
+    (dict(g=-1), EINVAL), (dict(scale=0.0), EINVAL), (dict(scale=-1.0), EINVAL),
+    (dict(scale=float("nan")), EINVAL), (dict(scale=float("inf")), EINVAL), (dict(bias=float("nan")), EINVAL),
+    (dict(d=96), EUNSUP), (dict(d=256), EUNSUP), (dict(dtype=7), EUNSUP),
+    (dict(q=P + 8), EALIGN), (dict(o=P + 2), EALIGN), (dict(lse=P + 2), EALIGN),
+    (dict(n=2**31 - 100), EINVAL),
+])
+def test_prefill_rejects(kw, want):
+    assert _prefill(**kw) == want
+
+
+def _append(**kw):
+    a = dict(kc=P, vc=P, kn=P, vn=P, pos=P, batch=1, heads=1, t=1, d=128, w=8, g=0, dtype=1)
+    a.update(kw)
+    return swa.lib().swa_kv_append(a["kc"], a["vc"], a["kn"], a["vn"], a["pos"], a["batch"], a["heads"], a["t"],
+                                   a["d"], a["w"], a["g"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(kc=None), EINVAL), (dict(pos=None), EINVAL), (dict(batch=0), EINVAL), (dict(t=-1), EINVAL),
+    (dict(w=0), EINVAL), (dict(g=-2), EINVAL), (dict(d=32), EUNSUP), (dict(dtype=3), EUNSUP),
+    (dict(kn=P + 4), EALIGN), (dict(pos=P + 4), EALIGN),
+    (dict(t=0), OK),  # nothing to write: returns without launching
+])
+def test_kv_append_rejects(kw, want):
+    assert _append(**kw) == want
+
+
+def _decode(**kw):
+    a = dict(q=P, kc=P, vc=P, pos=P, o=P, lse=None, batch=64, heads=32, d=128, w=4096, g=4,
+             scale=0.125, bias=0.0, dtype=1, ws=None, wsb=0)
+    a.update(kw)
+    return swa.lib().swa_decode_fwd(a["q"], a["kc"], a["vc"], a["pos"], a["o"], a["lse"], a["batch"], a["heads"],
+                                    a["d"], a["w"], a["g"], a["scale"], a["bias"], a["dtype"], a["ws"], a["wsb"],
+                                    None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), EINVAL), (dict(kc=None), EINVAL), (dict(pos=None), EINVAL), (dict(o=None), EINVAL),
+    (dict(batch=0), EINVAL), (dict(w=0), EINVAL), (dict(g=-1), EINVAL), (dict(scale=0.0), EINVAL),
+    (dict(d=80), EUNSUP), (dict(dtype=2), EUNSUP), (dict(vc=P + 8), EALIGN), (dict(lse=P + 1), EALIGN),
+    (dict(batch=1, heads=1), EWS),            # small problem splits the cache -> needs a workspace
+    (dict(batch=1, heads=1, ws=P, wsb=8), EWS),
+])
+def test_decode_rejects(kw, want):
+    assert _decode(**kw) == want
+
+
+def test_decode_workspace_sizes():
+    assert swa.decode_workspace_bytes(64, 32, 128, 4096, 4) == 0      # enough (batch, head) pairs
+    need = swa.decode_workspace_bytes(1, 1, 128, 4096, 4)
+    assert need > 0 and need % 16 == 0
+    assert swa.decode_workspace_bytes(1, 1, 96, 4096, 4) == 0           # unsupported d: nothing to size

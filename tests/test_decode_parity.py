@@ -1,0 +1,172 @@
+"""HIP kv_append and decode kernels (through the C ABI) against the oracle.
+
+kv_append must equal the token-by-token cache model bit for bit.  decode is
+compared with the oracle's decode over the logical sequence (fp32 1e-4,
+bf16 2e-2 max-abs); the oracle never reads the cache layout itself.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_causal_band_amd as swa
+from block_sparse_causal_band_amd import synth
+from oracle import cache_model
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 1e-4
+BF16_TOL = 2e-2
+
+
+def _dev():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    return torch.device("cuda")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("w,g,T,starts", [
+    (8, 0, 1, [0, 5, 17]), (8, 4, 3, [0, 2, 40]), (8, 4, 13, [0, 1, 9]), (5, 3, 30, [0, 2, 7]),
+    (64, 4, 64, [0, 64, 1000]), (16, 0, 40, [3, 0, 100]),
+])
+def test_kv_append_bit_exact(dtype, d, w, g, T, starts):
+    dev = _dev()
+    B, H = len(starts), 2
+    kc0 = synth.normal((B, H, g + w, d), seed=1, dtype=dtype)
+    vc0 = synth.normal((B, H, g + w, d), seed=2, dtype=dtype)
+    kn = synth.normal((B, H, T, d), seed=3, dtype=dtype)
+    vn = synth.normal((B, H, T, d), seed=4, dtype=dtype)
+    pos = torch.tensor(starts, dtype=torch.int64)
+    ref_k, ref_v = kc0.clone(), vc0.clone()
+    cache_model.append(ref_k, ref_v, kn, vn, pos.tolist(), w, g)
+    gk, gv = kc0.to(dev), vc0.to(dev)
+    swa.kv_append(gk, gv, kn.to(dev), vn.to(dev), pos.to(dev), w=w, g=g)
+    torch.cuda.synchronize()
+    assert torch.equal(gk.cpu(), ref_k) and torch.equal(gv.cpu(), ref_v)
+
+
+def _decode_vs_oracle(orc, q, kc, vc, pos, w, g, beta, units=None, tol=None):
+    """GPU decode vs the oracle; the oracle receives logical rows (position,
+    k, v) that the cache model says the cache supplies for each query."""
+    B, H, d = q.shape
+    o, lse = swa.decode(q, kc, vc, pos, w=w, g=g, sink_bias=beta, return_lse=True)
+    torch.cuda.synchronize()
+    if units is None:
+        units = [(b, h) for b in range(B) for h in range(H)]
+    if tol is None:
+        tol = BF16_TOL if q.dtype == torch.bfloat16 else F32_TOL
+    pos_h = pos.cpu().tolist()
+    qs, ps, kps, ks, vs = [], [], [], [], []
+    nk = g + w
+    for b, h in units:
+        p = pos_h[b]
+        positions, rows = cache_model.logical_rows(p, w, g)
+        kp = np.full(nk, -1, dtype=np.int64)
+        kp[:len(positions)] = positions
+        rows_t = torch.as_tensor(rows, device=kc.device)
+        kk = torch.zeros(nk, d, dtype=torch.float64)
+        vv = torch.zeros(nk, d, dtype=torch.float64)
+        kk[:len(rows)] = kc[b, h].index_select(0, rows_t).double().cpu()
+        vv[:len(rows)] = vc[b, h].index_select(0, rows_t).double().cpu()
+        qs.append(q[b, h].double().cpu()); ps.append(p); kps.append(kp); ks.append(kk); vs.append(vv)
+    ro, rl = orc.decode(torch.stack(qs), ps, np.stack(kps), torch.stack(ks), torch.stack(vs),
+                        w=w, g=g, beta=beta)
+    go = torch.stack([o[b, h] for b, h in units]).float().cpu().numpy()
+    gl = torch.stack([lse[b, h] for b, h in units]).cpu().numpy()
+    err = float(np.max(np.abs(go - ro)))
+    assert np.all(np.isfinite(go))
+    assert err <= tol, f"decode max-abs {err:.3g} > {tol}"
+    assert float(np.max(np.abs(gl - rl))) <= (1e-4 if q.dtype == torch.float32 else 2e-2)
+    return err
+
+
+EDGE_POS = lambda w, g: sorted({0, 1, 2, 3, g, w - 2, w - 1, w, w + 1, w + 2, w + g - 1, w + g, 3 * w + 7})
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("w,g,beta", [(16, 0, 0.0), (16, 4, 0.0), (100, 4, 4.0), (7, 9, -1.0), (1, 2, 1.0)])
+def test_decode_through_appended_cache(orc, dtype, d, w, g, beta):
+    """Fill the cache by kv_append with positions 0..p of a logical sequence,
+    then decode at p: every edge position of the ring and the sinks."""
+    dev = _dev()
+    positions = [p for p in EDGE_POS(w, g) if p >= 0]
+    B, H = len(positions), 3
+    n = max(positions) + 1
+    kseq = synth.normal((B, H, n, d), seed=31, dtype=dtype, device="cpu")
+    vseq = synth.normal((B, H, n, d), seed=32, dtype=dtype, device="cpu")
+    q = synth.normal((B, H, d), seed=33, dtype=dtype, device="cpu").to(dev)
+    kc = torch.zeros(B, H, g + w, d, dtype=dtype, device=dev)
+    vc = torch.zeros_like(kc)
+    # append each batch entry's prefix 0..p in one multi-token call
+    for b, p in enumerate(positions):
+        one = torch.zeros(1, dtype=torch.int64, device=dev)
+        swa.kv_append(kc[b:b + 1], vc[b:b + 1], kseq[b:b + 1, :, :p + 1].contiguous().to(dev),
+                      vseq[b:b + 1, :, :p + 1].contiguous().to(dev), one, w=w, g=g)
+    pos = torch.tensor(positions, dtype=torch.int64, device=dev)
+    _decode_vs_oracle(orc, q, kc, vc, pos, w, g, beta)
+    # and equals row p of the oracle's prefill over the logical sequence
+    o_gpu = swa.decode(q, kc, vc, pos, w=w, g=g, sink_bias=beta).float().cpu().numpy()
+    tol = BF16_TOL if dtype == torch.bfloat16 else F32_TOL
+    for b, p in enumerate(positions):
+        qseq = torch.zeros(H, p + 1, d, dtype=torch.float64)
+        qseq[:, p] = q[b].double().cpu()
+        ro, _ = orc.prefill(qseq, kseq[b, :, :p + 1], vseq[b, :, :p + 1], w=w, g=g, beta=beta, rows=[p])
+        assert float(np.max(np.abs(o_gpu[b] - ro[:, 0]))) <= tol
+
+
+@pytest.mark.parametrize("B,H", [(1, 1), (2, 3), (8, 128)])
+def test_decode_split_and_unsplit(orc, B, H):
+    """Few (batch, head) pairs split the cache over workgroups and merge by
+    LSE; many pairs do not.  Both paths against the oracle."""
+    dev = _dev()
+    w, g, d = 700, 4, 128
+    q, kc, vc, pos = synth.decode_problem(B, H, d, g + w, w, 5 * w, torch.bfloat16, seed=41, device=dev)
+    units = [(b, h) for b in range(B) for h in range(H)][:64]
+    _decode_vs_oracle(orc, q, kc, vc, pos, w, g, 0.5, units=units)
+
+
+def test_decode_negative_position_gives_nan():
+    dev = _dev()
+    q, kc, vc, _ = synth.decode_problem(2, 2, 128, 20, 16, 16, torch.bfloat16, seed=1, device=dev)
+    pos = torch.tensor([-1, 30], dtype=torch.int64, device=dev)
+    o = swa.decode(q, kc, vc, pos, w=16, g=4)
+    torch.cuda.synchronize()
+    assert torch.isnan(o[0].float()).all() and torch.isfinite(o[1].float()).all()
+
+
+def test_decode_equals_prefill_row():
+    """Decode at p over a cache filled by kv_append equals prefill row p (GPU vs GPU)."""
+    dev = _dev()
+    B, H, n, d, w, g = 1, 4, 1500, 128, 512, 4
+    q, k, v = synth.qkv(B, H, n, d, torch.bfloat16, seed=51, device=dev)
+    o_pre = swa.prefill(q, k, v, w=w, g=g, sink_bias=4.0)
+    kc = torch.zeros(B, H, g + w, d, dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    zero = torch.zeros(B, dtype=torch.int64, device=dev)
+    swa.kv_append(kc, vc, k, v, zero, w=w, g=g)
+    pos = torch.full((B,), n - 1, dtype=torch.int64, device=dev)
+    o_dec = swa.decode(q[:, :, n - 1].contiguous(), kc, vc, pos, w=w, g=g, sink_bias=4.0)
+    torch.cuda.synchronize()
+    assert float((o_dec.float() - o_pre[:, :, n - 1].float()).abs().max()) <= BF16_TOL
+
+
+def test_decode_full_size_sampled(orc):
+    """Rolling-cache decode workload: batch 64, 32 heads, d=128, w=4096, g=4,
+    positions uniform in [4096, 131072]; 64 sampled (batch, head) pairs."""
+    dev = _dev()
+    B, H, d, w, g = 64, 32, 128, 4096, 4
+    q, kc, vc, pos = synth.decode_problem(B, H, d, g + w, w, 131072, torch.bfloat16, seed=4, device=dev)
+    rng = np.random.default_rng(4)
+    units = sorted({(int(b), int(h)) for b, h in zip(rng.integers(0, B, 64), rng.integers(0, H, 64))})
+    err = _decode_vs_oracle(orc, q, kc, vc, pos, w, g, 0.0, units=units)
+    print(f"decode full size: max-abs {err:.3g} over {len(units)} units")
+
+
+def test_decode_deterministic():
+    dev = _dev()
+    q, kc, vc, pos = synth.decode_problem(4, 8, 128, 1028, 1024, 9000, torch.bfloat16, seed=7, device=dev)
+    a = swa.decode(q, kc, vc, pos, w=1024, g=4)
+    b = swa.decode(q, kc, vc, pos, w=1024, g=4)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
