@@ -11,6 +11,20 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0
+// in hardware, so tails need no branches.  Word 3 is the gfx9-family raw
+// (untyped, 32-bit data format) descriptor setting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+// 16-byte load at byte offset voff (checked against the resource size).
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+    return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
 // 16-byte streaming load (non-temporal: the data is read once).
 __device__ __forceinline__ uint4 load_stream16(const void *p) {
     u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));

@@ -61,48 +61,61 @@ struct PrefillCfg {
     static_assert(kVBlocksAll % kThreads == 0 || kVBlocksAll < kThreads, "V tile split");
 };
 
-// Global -> registers: one K/V tile (rows >= n read as zero, never loaded).
+// One K/V tile: HBM -> registers (buffer loads; rows >= n come back as 0
+// from the hardware range check) -> LDS (K row-major [key][d], V transposed
+// [d][key]).  Per-thread offsets are fixed for the whole run; only the row
+// of the tile start changes, which moves the buffer base (scalar work).
+// A thread moves 4 keys x one 16-byte column chunk of V; the key group is the
+// fastest-varying index across lanes, so the 16 lanes that write one V^T row
+// together cover 128 contiguous bytes: with 32 four-byte LDS banks those
+// writes, the K writes and both MFMA operand reads are free of bank conflicts
+// (with the chunk index fastest instead, the transposed writes hit rows eight
+// apart and collide 8-way).
 template <bool BF16, int D>
-struct TileRegs {
+struct TileLoader {
     using C = PrefillCfg<BF16, D>;
+    using T = typename C::T;
+    static constexpr uint32_t kRowBytes = D * C::kElem;
     uint4 k[C::kKChunks];
     uint4 v[C::kVBlocks][4];
 
-    __device__ __forceinline__ void load(const typename C::T *kb, const typename C::T *vb,
-                                         int k0, int n, int tid) {
+    __device__ __forceinline__ void load(const T *kb, const T *vb, int k0, int n, int tid) {
+        const uint32_t bytes = (uint32_t)(n - k0) * kRowBytes;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + (size_t)k0 * D, bytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + (size_t)k0 * D, bytes);
 #pragma unroll
         for (int i = 0; i < C::kKChunks; ++i) {
-            int id = tid + kThreads * i;
-            int row = id / C::kCPR, cc = id % C::kCPR;
-            k[i] = (k0 + row < n) ? *reinterpret_cast<const uint4 *>(kb + (size_t)(k0 + row) * D + cc * C::kEPC)
-                                  : make_uint4(0, 0, 0, 0);
+            const int id = tid + kThreads * i;
+            const int row = id / C::kCPR, cc = id % C::kCPR;
+            k[i] = buffer_load16(rk, row * kRowBytes + cc * 16);
         }
 #pragma unroll
         for (int i = 0; i < C::kVBlocks; ++i) {
-            int id = tid + kThreads * i;
-            int cg = id % C::kCPR, kg = id / C::kCPR;
+            const int id = tid + kThreads * i;
+            const int kg = id % (kBK / 4), cg = id / (kBK / 4);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                int row = k0 + 4 * kg + rr;
-                v[i][rr] = (id < C::kVBlocksAll && row < n) ? *reinterpret_cast<const uint4 *>(vb + (size_t)row * D + cg * C::kEPC)
-                                     : make_uint4(0, 0, 0, 0);
+                // ids past the tile's V blocks read past the resource: zeros, unused
+                const uint32_t off = (id < C::kVBlocksAll) ? (4 * kg + rr) * kRowBytes + cg * 16 : 0xfffffff0u;
+                v[i][rr] = buffer_load16(rv, off);
             }
         }
     }
 
-    // Registers -> LDS: K row-major [key][d]; V transposed [d][key].
-    __device__ __forceinline__ void store(typename C::T *ks, typename C::T *vts, int tid) const {
+    __device__ __forceinline__ void store(T *ks, T *vts, int tid) const {
 #pragma unroll
         for (int i = 0; i < C::kKChunks; ++i) {
-            int id = tid + kThreads * i;
-            int row = id / C::kCPR, cc = id % C::kCPR;
+            const int id = tid + kThreads * i;
+            const int row = id / C::kCPR, cc = id % C::kCPR;
             *reinterpret_cast<uint4 *>(ks + row * C::kKStride + cc * C::kEPC) = k[i];
         }
 #pragma unroll
         for (int i = 0; i < C::kVBlocks; ++i) {
-            int id = tid + kThreads * i;
-            if (id >= C::kVBlocksAll) break;
-            int cg = id % C::kCPR, kg = id / C::kCPR;
+            const int id = tid + kThreads * i;
+            if constexpr (C::kVBlocksAll % kThreads != 0) {
+                if (id >= C::kVBlocksAll) break;
+            }
+            const int kg = id % (kBK / 4), cg = id / (kBK / 4);
             const uint32_t *r0 = reinterpret_cast<const uint32_t *>(&v[i][0]);
             const uint32_t *r1 = reinterpret_cast<const uint32_t *>(&v[i][1]);
             const uint32_t *r2 = reinterpret_cast<const uint32_t *>(&v[i][2]);
@@ -111,18 +124,17 @@ struct TileRegs {
                 // 4 keys x 8 columns -> 8 columns of 4 keys (8 bytes each)
 #pragma unroll
                 for (int cc = 0; cc < 8; ++cc) {
-                    uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
-                    uint32_t lo = __builtin_amdgcn_perm(r1[cc >> 1], r0[cc >> 1], sel);
-                    uint32_t hi = __builtin_amdgcn_perm(r3[cc >> 1], r2[cc >> 1], sel);
+                    const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
+                    const uint32_t lo = __builtin_amdgcn_perm(r1[cc >> 1], r0[cc >> 1], sel);
+                    const uint32_t hi = __builtin_amdgcn_perm(r3[cc >> 1], r2[cc >> 1], sel);
                     *reinterpret_cast<uint2 *>(vts + (cg * 8 + cc) * C::kVStride + 4 * kg) = make_uint2(lo, hi);
                 }
             } else {
                 // 4 keys x 4 columns -> 4 columns of 4 keys (16 bytes each)
 #pragma unroll
-                for (int cc = 0; cc < 4; ++cc) {
+                for (int cc = 0; cc < 4; ++cc)
                     *reinterpret_cast<uint4 *>(vts + (cg * 4 + cc) * C::kVStride + 4 * kg) =
                         make_uint4(r0[cc], r1[cc], r2[cc], r3[cc]);
-                }
             }
         }
     }
@@ -155,21 +167,33 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void prefill_kernel(
     const int qi = q0 + wave * 32 + lr;  // this lane's query position
     const BandRange band = band_range(q0, q1, w, g, kBK);
     const int ntiles = band.count();
+    // A score more than tau above the running max forces a rescale; below
+    // that the stale max is kept (probabilities stay <= 2^8, exact after the
+    // final normalisation).
+    const float tau = 8.f / c2;
 
     // ---- Q of this wave's 32 rows as the B operand (kept in VGPRs) ----
     constexpr int kQRegs = BF16 ? D / 16 : D / 2;
     using QReg = typename std::conditional<BF16, bf16x8, float>::type;
     QReg qf[kQRegs];
-    if constexpr (BF16) {
+    {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + (size_t)q0 * D, (uint32_t)(n - q0) * D * C::kElem);
+        const uint32_t rowoff = (uint32_t)(wave * 32 + lr) * D * C::kElem;
+        if constexpr (BF16) {
 #pragma unroll
-        for (int c = 0; c < kQRegs; ++c) {
-            uint4 x = (qi < n) ? *reinterpret_cast<const uint4 *>(Q + (size_t)qi * D + 16 * c + 8 * lh)
-                               : make_uint4(0, 0, 0, 0);
-            qf[c] = __builtin_bit_cast(bf16x8, x);
+            for (int c = 0; c < kQRegs; ++c)
+                qf[c] = __builtin_bit_cast(bf16x8, buffer_load16(rq, rowoff + (16 * c + 8 * lh) * 2));
+        } else {
+#pragma unroll
+            for (int c4 = 0; c4 < kQRegs / 4; ++c4) {
+                // lane half lh takes the odd/even d of each pair: d = 2c + lh
+                const uint4 a = buffer_load16(rq, rowoff + (8 * c4) * 4);
+                const uint4 b = buffer_load16(rq, rowoff + (8 * c4 + 4) * 4);
+                const uint32_t e[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) qf[4 * c4 + j] = __uint_as_float(lh ? e[2 * j + 1] : e[2 * j]);
+            }
         }
-    } else {
-#pragma unroll
-        for (int c = 0; c < kQRegs; ++c) qf[c] = (qi < n) ? Q[(size_t)qi * D + 2 * c + lh] : 0.f;
     }
 
     f32x16 oacc[D / 32];
@@ -177,21 +201,24 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void prefill_kernel(
     for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[cb][r] = 0.f;
-    float m_run = kNegInf;  // running row max (raw q.k units, bias included)
-    float l_run = 0.f;      // running row sum of this lane's half of the keys
+    float m_run = kNegInf;  // reference row max (raw q.k units, bias included)
+    float negm = 0.f;       // -m_run * c2, or 0 while m_run = -inf
+    float l_run = 0.f;      // row sum over this lane's half of the keys
 
-    TileRegs<BF16, D> regs;
-    regs.load(K, V, band.block(0) * kBK, n, tid);
-    regs.store(smem, smem + C::kKElems, tid);
+    TileLoader<BF16, D> ld;
+    ld.load(K, V, band.block(0) * kBK, n, tid);
+    ld.store(smem, smem + C::kKElems, tid);
     __syncthreads();
 
-    for (int t = 0; t < ntiles; ++t) {
-        const int cur = t & 1;
-        const T *Ks = smem + cur * C::kStage;
+    // One tile of keys: K/V of tile t are in LDS stage `stage`; the loads of
+    // tile t+1 go out first and land in the other stage at the end.
+    auto do_tile = [&](int t, int stage, auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        const T *Ks = smem + stage * C::kStage;
         const T *Vts = Ks + C::kKElems;
         const int k0 = band.block(t) * kBK;
         const bool has_next = (t + 1 < ntiles);
-        if (has_next) regs.load(K, V, band.block(t + 1) * kBK, n, tid);
+        if (has_next) ld.load(K, V, band.block(t + 1) * kBK, n, tid);
 
         // ---- S^T = K Q^T for the two 32-key sub-blocks ----
         f32x16 s[2];
@@ -203,7 +230,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void prefill_kernel(
                 const T *krow = Ks + (32 * sb + lr) * C::kKStride + 8 * lh;
 #pragma unroll
                 for (int c = 0; c < D / 16; ++c) {
-                    bf16x8 a = *reinterpret_cast<const bf16x8 *>(krow + 16 * c);
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(krow + 16 * c);
                     s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[sb], 0, 0, 0);
                 }
             } else {
@@ -215,65 +242,79 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void prefill_kernel(
         }
         // s[sb][r] = q_qi . k_j with j = k0 + 32 sb + 8 (r/4) + 4 lh + r%4
 
-        // ---- exact masking on EDGE tiles ----
-        const bool full = tile_full(q0, q1, k0, k0 + kBK - 1, n, w, g);
-        if (!full) {
+        // ---- exact masking (and sink bias) on tiles the band or sinks cut ----
+        if constexpr (MASKED) {
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    int j = k0 + 32 * sb + 8 * (r >> 2) + 4 * lh + (r & 3);
-                    float x = s[sb][r] + (j < g ? bias_raw : 0.f);
+                    const int j = k0 + 32 * sb + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    const float x = s[sb][r] + (j < g ? bias_raw : 0.f);
                     s[sb][r] = pair_attended(qi, j, n, w, g) ? x : kNegInf;
                 }
         }
 
-        // ---- online softmax (row = lane & 31; halves merged by a swap) ----
+        // ---- online softmax with a lazily moved reference max ----
         float mx = kNegInf;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
         mx = half_swap_max(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = fast_exp2((m_run - m_use) * c2);
-        const float neg = -m_use * c2;
-        float lsum = 0.f;
+        if (__any(mx > m_run + tau)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_run - m_new) * c2);
+            m_run = m_new;
+            negm = (m_new == kNegInf) ? 0.f : -m_new * c2;
+            l_run *= alpha;
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
+            for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float p = fast_exp2(fmaf(s[sb][r], c2, neg));
-                s[sb][r] = p;
-                lsum += p;
-            }
-        l_run = l_run * alpha + lsum;
-        m_run = m_new;
-#pragma unroll
-        for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+                for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+        }
 
-        // ---- O^T += V^T P^T ----
+        // ---- P = exp2(s c2 - m c2); O^T += V^T P^T ----
         if constexpr (BF16) {
             bf16x8 pb[4];
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) pb[kc][e] = static_cast<__bf16>(s[kc >> 1][8 * (kc & 1) + e]);
+                for (int e = 0; e < 8; ++e)
+                    pb[kc][e] = static_cast<__bf16>(fast_exp2(fmaf(s[kc >> 1][8 * (kc & 1) + e], c2, negm)));
+            // row sum of the bf16 probabilities the value product uses
+            const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+            float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) {
+                const bf16x2 p01 = {pb[kc][0], pb[kc][1]}, p23 = {pb[kc][2], pb[kc][3]};
+                const bf16x2 p45 = {pb[kc][4], pb[kc][5]}, p67 = {pb[kc][6], pb[kc][7]};
+                ls0 = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, ls0, false);
+                ls1 = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, ls1, false);
+                ls0 = __builtin_amdgcn_fdot2_f32_bf16(p45, ones, ls0, false);
+                ls1 = __builtin_amdgcn_fdot2_f32_bf16(p67, ones, ls1, false);
+            }
+            l_run += ls0 + ls1;
 #pragma unroll
             for (int cb = 0; cb < D / 32; ++cb) {
                 const T *vrow = Vts + (32 * cb + lr) * C::kVStride + 4 * lh;
 #pragma unroll
                 for (int kc = 0; kc < 4; ++kc) {
-                    uint2 lo = *reinterpret_cast<const uint2 *>(vrow + 16 * kc);
-                    uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 16 * kc + 8);
-                    bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                    const uint2 lo = *reinterpret_cast<const uint2 *>(vrow + 16 * kc);
+                    const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 16 * kc + 8);
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
                     oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc], oacc[cb], 0, 0, 0);
                 }
             }
         } else {
+            float lsum = 0.f;
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    s[sb][r] = fast_exp2(fmaf(s[sb][r], c2, negm));
+                    lsum += s[sb][r];
+                }
+            l_run += lsum;
 #pragma unroll
             for (int cb = 0; cb < D / 32; ++cb) {
                 const T *vrow = Vts + (32 * cb + lr) * C::kVStride + 4 * lh;
@@ -281,15 +322,34 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void prefill_kernel(
                 for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        float a = vrow[32 * sb + 8 * (r >> 2) + (r & 3)];
+                        const float a = vrow[32 * sb + 8 * (r >> 2) + (r & 3)];
                         oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[sb][r], oacc[cb], 0, 0, 0);
                     }
             }
         }
 
-        if (has_next) regs.store(smem + (cur ^ 1) * C::kStage, smem + (cur ^ 1) * C::kStage + C::kKElems, tid);
+        if (has_next) {
+            T *nxt = smem + (stage ^ 1) * C::kStage;
+            ld.store(nxt, nxt + C::kKElems, tid);
+        }
         __syncthreads();
+    };
+
+    // Visiting order: sink tiles and the band's lower-edge tiles (masked),
+    // then the run of FULL tiles in a tight loop of its own, then the
+    // diagonal tiles (masked).  The FULL run is contiguous in key-block order.
+    int t_full_lo = ntiles, t_full_hi = ntiles;  // FULL tiles are [t_full_lo, t_full_hi)
+    for (int t = 0; t < ntiles; ++t) {
+        const int kb = band.block(t);
+        if (tile_full(q0, q1, kb * kBK, kb * kBK + kBK - 1, n, w, g)) {
+            if (t_full_lo == ntiles) t_full_lo = t;
+            t_full_hi = t + 1;
+        }
     }
+    int t = 0, stage = 0;
+    for (; t < t_full_lo; ++t, stage ^= 1) do_tile(t, stage, std::true_type{});
+    for (; t < t_full_hi; ++t, stage ^= 1) do_tile(t, stage, std::false_type{});
+    for (; t < ntiles; ++t, stage ^= 1) do_tile(t, stage, std::true_type{});
 
     // ---- epilogue: normalise, store O (and LSE) ----
     const float l_tot = half_swap_sum(l_run);
@@ -300,9 +360,9 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void prefill_kernel(
         for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-                int c = 32 * cb + 8 * gq + 4 * lh;
-                float x0 = oacc[cb][4 * gq + 0] * inv, x1 = oacc[cb][4 * gq + 1] * inv;
-                float x2 = oacc[cb][4 * gq + 2] * inv, x3 = oacc[cb][4 * gq + 3] * inv;
+                const int c = 32 * cb + 8 * gq + 4 * lh;
+                const float x0 = oacc[cb][4 * gq + 0] * inv, x1 = oacc[cb][4 * gq + 1] * inv;
+                const float x2 = oacc[cb][4 * gq + 2] * inv, x3 = oacc[cb][4 * gq + 3] * inv;
                 if constexpr (BF16) {
                     *reinterpret_cast<uint2 *>(O + c) = make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
                 } else {
