@@ -15,18 +15,31 @@
 //  * the workgroup visits only the key tiles of its band and sink blocks
 //    (schedule.h), 64 keys per tile, double-buffered in LDS;
 //  * both products run on the matrix cores with the 32x32 MFMA shapes:
-//      S^T = K Q^T   (A = K tile from LDS, B = the wave's Q held in VGPRs)
-//      O^T += V^T P^T (A = V tile stored transposed in LDS, B = P in VGPRs)
+//      S^T = K Q^T    (A = K tile from LDS, B = the wave's Q held in VGPRs)
+//      O^T += V^T P^T (A = V tile from LDS read transposed, B = P in VGPRs)
 //    Computing the transposes makes the MFMA result layout put one query row
 //    per lane (lanes l and l+32 share a row), so the online-softmax row max
 //    and row sum are in-register reductions plus one permlane32 swap, the
 //    probabilities P feed the second MFMA straight from the first one's
 //    accumulators, and the output rescale needs no cross-lane traffic;
-//  * FULL tiles skip masking; EDGE tiles (band edges, sinks, the ragged tail)
-//    evaluate the exact per-pair predicate and set excluded scores to -inf;
+//  * tiles that the window edge, a sink or the end of the sequence cuts are
+//    masked pair by pair (excluded scores -> -inf); the run of FULL tiles in
+//    between skips masking in a loop of its own;
 //  * scores stay in raw q.k units; exp2 with scale*log2(e) folded into one
-//    FMA per score.  A row with no attended key yet keeps m = -inf and is
-//    guarded so that no -inf - -inf is ever formed.
+//    FMA per score.  The reference max only moves when a score exceeds it by
+//    more than 2^8 in probability, so the O rescale is rare.  A row with no
+//    attended key yet keeps m = -inf and is guarded so that no -inf - -inf is
+//    ever formed.
+//
+// bf16 path: K and V tiles go HBM -> LDS by buffer loads that write LDS
+// directly (16 bytes per lane, out-of-range rows come back as zeros), so no
+// VGPRs stage them.  K is stored in 64-byte column blocks with an XOR swizzle
+// of its 16-byte chunks so that the 32 rows one MFMA operand read touches hit
+// distinct banks; V is stored row-major and its transposed MFMA operand is
+// read with ds_read_b64_tr_b16 (each 16-lane group of that instruction
+// transposes 4x4 blocks of 16-bit values across lanes).
+// fp32 path: tiles are staged through VGPRs and V is transposed on the way
+// into LDS; it exists for fp32 parity, not for speed.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -41,158 +54,376 @@ constexpr int kBQ = 128;      // query rows per workgroup (4 waves x 32)
 constexpr int kBK = 64;       // keys per tile (2 MFMA sub-blocks of 32)
 constexpr int kThreads = 256;
 
-template <bool BF16, int D>
-struct PrefillCfg {
-    using T = typename std::conditional<BF16, uint16_t, float>::type;
-    static constexpr int kElem = BF16 ? 2 : 4;
-    static constexpr int kEPC = 16 / kElem;            // elements per 16-byte chunk
-    static constexpr int kCPR = D / kEPC;               // chunks per K/V row
-    static constexpr int kKPad = BF16 ? 8 : 4;          // K row pad (elements)
-    static constexpr int kVPad = 4;                     // V^T row pad (elements)
-    static constexpr int kKStride = D + kKPad;
-    static constexpr int kVStride = kBK + kVPad;
-    static constexpr int kKElems = kBK * kKStride;
-    static constexpr int kVElems = D * kVStride;
-    static constexpr int kStage = kKElems + kVElems;
-    static constexpr int kKChunks = kBK * kCPR / kThreads;         // 16-B K loads per thread
-    static constexpr int kVBlocksAll = (kBK / 4) * kCPR;           // 4-key x 16-B V blocks per tile
-    static constexpr int kVBlocks = (kVBlocksAll + kThreads - 1) / kThreads;  // per thread
-    static_assert(kBK * kCPR % kThreads == 0, "K tile split");
-    static_assert(kVBlocksAll % kThreads == 0 || kVBlocksAll < kThreads, "V tile split");
-};
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define SWA_LDS __attribute__((address_space(3)))
 
-// One K/V tile: HBM -> registers (buffer loads; rows >= n come back as 0
-// from the hardware range check) -> LDS (K row-major [key][d], V transposed
-// [d][key]).  Per-thread offsets are fixed for the whole run; only the row
-// of the tile start changes, which moves the buffer base (scalar work).
-// A thread moves 4 keys x one 16-byte column chunk of V; the key group is the
-// fastest-varying index across lanes, so the 16 lanes that write one V^T row
-// together cover 128 contiguous bytes: with 32 four-byte LDS banks those
-// writes, the K writes and both MFMA operand reads are free of bank conflicts
-// (with the chunk index fastest instead, the transposed writes hit rows eight
-// apart and collide 8-way).
-template <bool BF16, int D>
-struct TileLoader {
-    using C = PrefillCfg<BF16, D>;
-    using T = typename C::T;
-    static constexpr uint32_t kRowBytes = D * C::kElem;
-    uint4 k[C::kKChunks];
-    uint4 v[C::kVBlocks][4];
+// 16-byte buffer load of every lane into LDS at lds + 16 * lane (one wave).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t *lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (SWA_LDS void *)lds, 16, voff, 0, 0, 0);
+}
+// ds_read_b64_tr_b16 at an LDS address.
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((SWA_LDS s16x4 *)p);
+}
 
-    __device__ __forceinline__ void load(const T *kb, const T *vb, int k0, int n, int tid) {
-        const uint32_t bytes = (uint32_t)(n - k0) * kRowBytes;
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + (size_t)k0 * D, bytes);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + (size_t)k0 * D, bytes);
+// ---------------------------------------------------------------------------
+// Pieces shared by both paths.  s[sb][r] holds q_qi . k_j for the key
+// j = k0 + 32 sb + 8 (r/4) + 4 lh + r%4 (the 32x32 MFMA result layout).
+
+// Exact predicate with sink bias on a cut tile.
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int qi, int k0, int lh, int n, int w, int g,
+                                          float bias_raw) {
 #pragma unroll
-        for (int i = 0; i < C::kKChunks; ++i) {
-            const int id = tid + kThreads * i;
-            const int row = id / C::kCPR, cc = id % C::kCPR;
-            k[i] = buffer_load16(rk, row * kRowBytes + cc * 16);
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int j = k0 + 32 * sb + 8 * (r >> 2) + 4 * lh + (r & 3);
+            const float x = s[sb][r] + (j < g ? bias_raw : 0.f);
+            s[sb][r] = pair_attended(qi, j, n, w, g) ? x : kNegInf;
         }
+}
+
+// Row max of the tile; moves the reference max (and rescales O and l) only
+// when some row of the wave would otherwise see a probability above 2^8.
+template <int NACC>
+__device__ __forceinline__ void update_max(const f32x16 (&s)[2], float &m_run, float &negm, float &l_run,
+                                           f32x16 (&oacc)[NACC], float c2, float tau) {
+    float mx = kNegInf;
 #pragma unroll
-        for (int i = 0; i < C::kVBlocks; ++i) {
-            const int id = tid + kThreads * i;
-            const int kg = id % (kBK / 4), cg = id / (kBK / 4);
+    for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                // ids past the tile's V blocks read past the resource: zeros, unused
-                const uint32_t off = (id < C::kVBlocksAll) ? (4 * kg + rr) * kRowBytes + cg * 16 : 0xfffffff0u;
-                v[i][rr] = buffer_load16(rv, off);
-            }
-        }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
+    mx = half_swap_max(mx);
+    if (__any(mx > m_run + tau)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_run - m_new) * c2);
+        m_run = m_new;
+        negm = (m_new == kNegInf) ? 0.f : -m_new * c2;
+        l_run *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < NACC; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
     }
+}
 
-    __device__ __forceinline__ void store(T *ks, T *vts, int tid) const {
+// Normalise and store O (and LSE) of this lane's query row.
+template <typename T, int D>
+__device__ __forceinline__ void store_rows(const f32x16 (&oacc)[D / 32], float m_run, float l_run, int qi, int n,
+                                           int lh, T *O, float *lse, float scale) {
+    const float l_tot = half_swap_sum(l_run);
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    if (qi >= n) return;
+    T *orow = O + (size_t)qi * D;
 #pragma unroll
-        for (int i = 0; i < C::kKChunks; ++i) {
-            const int id = tid + kThreads * i;
-            const int row = id / C::kCPR, cc = id % C::kCPR;
-            *reinterpret_cast<uint4 *>(ks + row * C::kKStride + cc * C::kEPC) = k[i];
-        }
+    for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
-        for (int i = 0; i < C::kVBlocks; ++i) {
-            const int id = tid + kThreads * i;
-            if constexpr (C::kVBlocksAll % kThreads != 0) {
-                if (id >= C::kVBlocksAll) break;
-            }
-            const int kg = id % (kBK / 4), cg = id / (kBK / 4);
-            const uint32_t *r0 = reinterpret_cast<const uint32_t *>(&v[i][0]);
-            const uint32_t *r1 = reinterpret_cast<const uint32_t *>(&v[i][1]);
-            const uint32_t *r2 = reinterpret_cast<const uint32_t *>(&v[i][2]);
-            const uint32_t *r3 = reinterpret_cast<const uint32_t *>(&v[i][3]);
-            if constexpr (BF16) {
-                // 4 keys x 8 columns -> 8 columns of 4 keys (8 bytes each)
-#pragma unroll
-                for (int cc = 0; cc < 8; ++cc) {
-                    const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
-                    const uint32_t lo = __builtin_amdgcn_perm(r1[cc >> 1], r0[cc >> 1], sel);
-                    const uint32_t hi = __builtin_amdgcn_perm(r3[cc >> 1], r2[cc >> 1], sel);
-                    *reinterpret_cast<uint2 *>(vts + (cg * 8 + cc) * C::kVStride + 4 * kg) = make_uint2(lo, hi);
-                }
+        for (int gq = 0; gq < 4; ++gq) {
+            const int c = 32 * cb + 8 * gq + 4 * lh;
+            const float x0 = oacc[cb][4 * gq + 0] * inv, x1 = oacc[cb][4 * gq + 1] * inv;
+            const float x2 = oacc[cb][4 * gq + 2] * inv, x3 = oacc[cb][4 * gq + 3] * inv;
+            if constexpr (std::is_same<T, uint16_t>::value) {
+                *reinterpret_cast<uint2 *>(orow + c) = make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
             } else {
-                // 4 keys x 4 columns -> 4 columns of 4 keys (16 bytes each)
-#pragma unroll
-                for (int cc = 0; cc < 4; ++cc)
-                    *reinterpret_cast<uint4 *>(vts + (cg * 4 + cc) * C::kVStride + 4 * kg) =
-                        make_uint4(r0[cc], r1[cc], r2[cc], r3[cc]);
+                *reinterpret_cast<float4 *>(orow + c) = make_float4(x0, x1, x2, x3);
             }
         }
+    if (lse != nullptr && lh == 0) lse[qi] = m_run * scale + logf(l_tot);
+}
+
+// FULL tiles are a contiguous run [t_lo, t_hi) of the visiting order.
+__device__ __forceinline__ void full_run(const BandRange &band, int q0, int q1, int n, int w, int g, int *t_lo,
+                                         int *t_hi) {
+    const int nt = band.count();
+    *t_lo = nt;
+    *t_hi = nt;
+    for (int t = 0; t < nt; ++t) {
+        const int kb = band.block(t);
+        if (tile_full(q0, q1, kb * kBK, kb * kBK + kBK - 1, n, w, g)) {
+            if (*t_lo == nt) *t_lo = t;
+            *t_hi = t + 1;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 path.
+template <int D>
+struct Bf16Tile {
+    static constexpr int kRowBytes = D * 2;
+    static constexpr int kTileBytes = kBK * kRowBytes;         // one K or V tile
+    static constexpr int kStageBytes = 2 * kTileBytes;         // K then V
+    static constexpr int kDmaPerWave = kTileBytes / 1024 / 4;  // 1 KB DMA loads per wave per tile
+    static_assert(kTileBytes % 4096 == 0, "tile split over 4 waves");
+    // LDS byte offset of K(key, 16-byte chunk c): 64-byte column block c/4,
+    // 64 bytes per key inside it, chunk position (c%4) ^ ((key/4)%4).
+    __device__ static constexpr uint32_t k_off(int key, int c) {
+        return (uint32_t)((c >> 2) * (kBK * 64) + key * 64 + 16 * ((c & 3) ^ ((key >> 2) & 3)));
+    }
+    // V(key, 8-byte piece p of 4 columns): same column blocks, no swizzle.
+    __device__ static constexpr uint32_t v_off(int key, int p) {
+        return (uint32_t)((p >> 3) * (kBK * 64) + key * 64 + 8 * (p & 7));
     }
 };
 
-template <bool BF16, int D>
-__global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void prefill_kernel(
-    const void *__restrict__ qp, const void *__restrict__ kp, const void *__restrict__ vp,
-    void *__restrict__ op, float *__restrict__ lsep, int n, int nqb, int w, int g,
-    float c2, float scale, float bias_raw, int total_wg) {
-    using C = PrefillCfg<BF16, D>;
-    using T = typename C::T;
-    __shared__ __attribute__((aligned(16))) T smem[2 * C::kStage];
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
+    const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp, const uint16_t *__restrict__ vp,
+    uint16_t *__restrict__ op, float *__restrict__ lsep, int n, int nqb, int w, int g, float c2, float scale,
+    float bias_raw, int total_wg) {
+    using L = Bf16Tile<D>;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * L::kStageBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 31;  // query row of this lane within the wave
     const int lh = lane >> 5;  // which half of the wave
 
     int unit, qb;
     workgroup_order(blockIdx.x, total_wg, nqb, &unit, &qb);
     const size_t base = (size_t)unit * n * D;
-    const T *Q = reinterpret_cast<const T *>(qp) + base;
-    const T *K = reinterpret_cast<const T *>(kp) + base;
-    const T *V = reinterpret_cast<const T *>(vp) + base;
+    const uint16_t *Q = qp + base;
+    const uint16_t *K = kp + base;
+    const uint16_t *V = vp + base;
 
     const int q0 = qb * kBQ;
     const int q1 = min(q0 + kBQ, n) - 1;
-    const int qi = q0 + wave * 32 + lr;  // this lane's query position
+    const int qi = q0 + wave * 32 + lr;
     const BandRange band = band_range(q0, q1, w, g, kBK);
     const int ntiles = band.count();
-    // A score more than tau above the running max forces a rescale; below
-    // that the stale max is kept (probabilities stay <= 2^8, exact after the
-    // final normalisation).
     const float tau = 8.f / c2;
 
     // ---- Q of this wave's 32 rows as the B operand (kept in VGPRs) ----
-    constexpr int kQRegs = BF16 ? D / 16 : D / 2;
-    using QReg = typename std::conditional<BF16, bf16x8, float>::type;
-    QReg qf[kQRegs];
+    bf16x8 qf[D / 16];
     {
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + (size_t)q0 * D, (uint32_t)(n - q0) * D * C::kElem);
-        const uint32_t rowoff = (uint32_t)(wave * 32 + lr) * D * C::kElem;
-        if constexpr (BF16) {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + (size_t)q0 * D, (uint32_t)(n - q0) * L::kRowBytes);
+        const uint32_t rowoff = (uint32_t)(wave * 32 + lr) * L::kRowBytes;
 #pragma unroll
-            for (int c = 0; c < kQRegs; ++c)
-                qf[c] = __builtin_bit_cast(bf16x8, buffer_load16(rq, rowoff + (16 * c + 8 * lh) * 2));
-        } else {
+        for (int c = 0; c < D / 16; ++c)
+            qf[c] = __builtin_bit_cast(bf16x8, buffer_load16(rq, rowoff + (16 * c + 8 * lh) * 2));
+    }
+
+    // ---- DMA of one K/V tile into a stage: each wave moves its share ----
+    // DMA load i of this wave fills LDS bytes [1 KB m, 1 KB (m+1)) of the tile,
+    // m = wave * kDmaPerWave + i: column block m/4, keys 16 (m%4) + lane/4,
+    // chunk position lane%4.  The global chunk that belongs there undoes the
+    // swizzle (K) or is the same chunk (V).
+    uint32_t dma_k[L::kDmaPerWave], dma_v[L::kDmaPerWave];
 #pragma unroll
-            for (int c4 = 0; c4 < kQRegs / 4; ++c4) {
-                // lane half lh takes the odd/even d of each pair: d = 2c + lh
-                const uint4 a = buffer_load16(rq, rowoff + (8 * c4) * 4);
-                const uint4 b = buffer_load16(rq, rowoff + (8 * c4 + 4) * 4);
-                const uint32_t e[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    for (int i = 0; i < L::kDmaPerWave; ++i) {
+        const int m = wave * L::kDmaPerWave + i;
+        const int key = 16 * (m & 3) + (lane >> 2);
+        const int pos = lane & 3;
+        const int ck = (m >> 2) * 4 + (pos ^ ((key >> 2) & 3));
+        const int cv = (m >> 2) * 4 + pos;
+        dma_k[i] = key * L::kRowBytes + 16 * ck;
+        dma_v[i] = key * L::kRowBytes + 16 * cv;
+    }
+    auto dma_tile = [&](int k0, int stage) {
+        const uint32_t bytes = (uint32_t)(n - k0) * L::kRowBytes;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + (size_t)k0 * D, bytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + (size_t)k0 * D, bytes);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) qf[4 * c4 + j] = __uint_as_float(lh ? e[2 * j + 1] : e[2 * j]);
+        for (int i = 0; i < L::kDmaPerWave; ++i) {
+            const int m = wave * L::kDmaPerWave + i;
+            uint8_t *dk = smem + stage * L::kStageBytes + m * 1024;
+            dma16(rk, dk, dma_k[i]);
+            dma16(rv, dk + L::kTileBytes, dma_v[i]);
+        }
+    };
+
+    // Per-lane LDS read offsets within a stage.
+    // K operand: row 32 sb + lr, 16-byte chunk 2c + lh; even and odd c differ
+    // in the chunk position, c/2 selects the column block.
+    const uint32_t koff_even = L::k_off(lr, lh);
+    const uint32_t koff_odd = L::k_off(lr, 2 + lh);
+    // V operand (transposed read): lane j of 16-lane group G supplies key
+    // 4 (G/2) + j/4 (on top of the chunk's key base) and the 8-byte piece of
+    // columns 16 (G%2) + 4 (j%4) .. +3; the instruction hands lane j of the
+    // group column 16 (G%2) + j of four consecutive keys.
+    const int grp = lane >> 4, jj = lane & 15;
+    const uint32_t voff = (uint32_t)L::kTileBytes + L::v_off(4 * (grp >> 1) + (jj >> 2), 4 * (grp & 1) + (jj & 3));
+
+    f32x16 oacc[D / 32];
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[cb][r] = 0.f;
+    float m_run = kNegInf, negm = 0.f, l_run = 0.f;
+
+    dma_tile(band.block(0) * kBK, 0);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA has landed
+    __syncthreads();
+
+    auto do_tile = [&](int t, int stage, auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        const uint8_t *sbase = smem + stage * L::kStageBytes;
+        const int k0 = band.block(t) * kBK;
+        if (t + 1 < ntiles) dma_tile(band.block(t + 1) * kBK, stage ^ 1);
+
+        // ---- S^T = K Q^T ----
+        f32x16 s[2];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) {
+                const uint32_t off = ((c & 1) ? koff_odd : koff_even) + (c >> 1) * (kBK * 64) + sb * 32 * 64;
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sbase + off);
+                s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[sb], 0, 0, 0);
             }
+        }
+        if constexpr (MASKED) mask_tile(s, qi, k0, lh, n, w, g, bias_raw);
+        update_max(s, m_run, negm, l_run, oacc, c2, tau);
+
+        // ---- P = exp2(s c2 - m c2), row sum, O^T += V^T P^T ----
+        bf16x8 pb[4];
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                pb[kc][e] = static_cast<__bf16>(fast_exp2(fmaf(s[kc >> 1][8 * (kc & 1) + e], c2, negm)));
+        const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+        float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+            const bf16x2 p01 = {pb[kc][0], pb[kc][1]}, p23 = {pb[kc][2], pb[kc][3]};
+            const bf16x2 p45 = {pb[kc][4], pb[kc][5]}, p67 = {pb[kc][6], pb[kc][7]};
+            ls0 = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, ls0, false);
+            ls1 = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, ls1, false);
+            ls0 = __builtin_amdgcn_fdot2_f32_bf16(p45, ones, ls0, false);
+            ls1 = __builtin_amdgcn_fdot2_f32_bf16(p67, ones, ls1, false);
+        }
+        l_run += ls0 + ls1;
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) {
+                // keys 16 kc + 4 lh + 0..3 (first read) and 16 kc + 8 + 4 lh + 0..3
+                const uint8_t *p0 = sbase + voff + cb * (kBK * 64) + (16 * kc) * 64;
+                const s16x4 lo = lds_read_tr16(p0);
+                const s16x4 hi = lds_read_tr16(p0 + 8 * 64);
+                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc], oacc[cb], 0, 0, 0);
+            }
+
+        __builtin_amdgcn_s_waitcnt(0);  // the next tile's DMA of this wave has landed
+        __syncthreads();
+    };
+
+    int t_lo, t_hi;
+    full_run(band, q0, q1, n, w, g, &t_lo, &t_hi);
+    int t = 0, stage = 0;
+    for (; t < t_lo; ++t, stage ^= 1) do_tile(t, stage, std::true_type{});
+    for (; t < t_hi; ++t, stage ^= 1) do_tile(t, stage, std::false_type{});
+    for (; t < ntiles; ++t, stage ^= 1) do_tile(t, stage, std::true_type{});
+
+    store_rows<uint16_t, D>(oacc, m_run, l_run, qi, n, lh, op + base, lsep ? lsep + (size_t)unit * n : nullptr,
+                            scale);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path (parity): VGPR-staged tiles, V transposed on the way into LDS.
+template <int D>
+struct F32Cfg {
+    static constexpr int kCPR = D / 4;        // 16-byte chunks per row
+    static constexpr int kKStride = D + 4;    // K row stride (floats)
+    static constexpr int kVStride = kBK + 4;  // V^T row stride (floats)
+    static constexpr int kKElems = kBK * kKStride;
+    static constexpr int kVElems = D * kVStride;
+    static constexpr int kStage = kKElems + kVElems;
+    static constexpr int kKChunks = kBK * kCPR / kThreads;
+    static constexpr int kVBlocks = (kBK / 4) * kCPR / kThreads;
+    static_assert(kBK * kCPR % kThreads == 0 && (kBK / 4) * kCPR % kThreads == 0, "tile split");
+};
+
+template <int D>
+struct F32TileLoader {
+    using C = F32Cfg<D>;
+    uint4 k[C::kKChunks];
+    uint4 v[C::kVBlocks][4];
+
+    __device__ __forceinline__ void load(const float *kb, const float *vb, int k0, int n, int tid) {
+        const uint32_t bytes = (uint32_t)(n - k0) * D * 4;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + (size_t)k0 * D, bytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + (size_t)k0 * D, bytes);
+#pragma unroll
+        for (int i = 0; i < C::kKChunks; ++i) {
+            const int id = tid + kThreads * i;
+            k[i] = buffer_load16(rk, (id / C::kCPR) * D * 4 + (id % C::kCPR) * 16);
+        }
+#pragma unroll
+        for (int i = 0; i < C::kVBlocks; ++i) {
+            const int id = tid + kThreads * i;
+            const int kg = id % (kBK / 4), cg = id / (kBK / 4);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) v[i][rr] = buffer_load16(rv, (4 * kg + rr) * D * 4 + cg * 16);
+        }
+    }
+    __device__ __forceinline__ void store(float *ks, float *vts, int tid) const {
+#pragma unroll
+        for (int i = 0; i < C::kKChunks; ++i) {
+            const int id = tid + kThreads * i;
+            *reinterpret_cast<uint4 *>(ks + (id / C::kCPR) * C::kKStride + (id % C::kCPR) * 4) = k[i];
+        }
+#pragma unroll
+        for (int i = 0; i < C::kVBlocks; ++i) {
+            const int id = tid + kThreads * i;
+            const int kg = id % (kBK / 4), cg = id / (kBK / 4);
+            const uint32_t *r0 = reinterpret_cast<const uint32_t *>(&v[i][0]);
+            const uint32_t *r1 = reinterpret_cast<const uint32_t *>(&v[i][1]);
+            const uint32_t *r2 = reinterpret_cast<const uint32_t *>(&v[i][2]);
+            const uint32_t *r3 = reinterpret_cast<const uint32_t *>(&v[i][3]);
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc)
+                *reinterpret_cast<uint4 *>(vts + (cg * 4 + cc) * C::kVStride + 4 * kg) =
+                    make_uint4(r0[cc], r1[cc], r2[cc], r3[cc]);
+        }
+    }
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
+    const float *__restrict__ qp, const float *__restrict__ kp, const float *__restrict__ vp,
+    float *__restrict__ op, float *__restrict__ lsep, int n, int nqb, int w, int g, float c2, float scale,
+    float bias_raw, int total_wg) {
+    using C = F32Cfg<D>;
+    __shared__ __attribute__((aligned(16))) float smem[2 * C::kStage];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int lr = lane & 31;
+    const int lh = lane >> 5;
+
+    int unit, qb;
+    workgroup_order(blockIdx.x, total_wg, nqb, &unit, &qb);
+    const size_t base = (size_t)unit * n * D;
+    const float *Q = qp + base;
+    const float *K = kp + base;
+    const float *V = vp + base;
+
+    const int q0 = qb * kBQ;
+    const int q1 = min(q0 + kBQ, n) - 1;
+    const int qi = q0 + wave * 32 + lr;
+    const BandRange band = band_range(q0, q1, w, g, kBK);
+    const int ntiles = band.count();
+    const float tau = 8.f / c2;
+
+    // Q as the B operand of 32x32x2 MFMAs: lane half lh holds d = 2c + lh
+    float qf[D / 2];
+    {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + (size_t)q0 * D, (uint32_t)(n - q0) * D * 4);
+        const uint32_t rowoff = (uint32_t)(wave * 32 + lr) * D * 4;
+#pragma unroll
+        for (int c4 = 0; c4 < D / 8; ++c4) {
+            const uint4 a = buffer_load16(rq, rowoff + (8 * c4) * 4);
+            const uint4 b = buffer_load16(rq, rowoff + (8 * c4 + 4) * 4);
+            const uint32_t e[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qf[4 * c4 + j] = __uint_as_float(lh ? e[2 * j + 1] : e[2 * j]);
         }
     }
 
@@ -201,201 +432,100 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void prefill_kernel(
     for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[cb][r] = 0.f;
-    float m_run = kNegInf;  // reference row max (raw q.k units, bias included)
-    float negm = 0.f;       // -m_run * c2, or 0 while m_run = -inf
-    float l_run = 0.f;      // row sum over this lane's half of the keys
+    float m_run = kNegInf, negm = 0.f, l_run = 0.f;
 
-    TileLoader<BF16, D> ld;
+    F32TileLoader<D> ld;
     ld.load(K, V, band.block(0) * kBK, n, tid);
     ld.store(smem, smem + C::kKElems, tid);
     __syncthreads();
 
-    // One tile of keys: K/V of tile t are in LDS stage `stage`; the loads of
-    // tile t+1 go out first and land in the other stage at the end.
     auto do_tile = [&](int t, int stage, auto masked_tag) {
         constexpr bool MASKED = decltype(masked_tag)::value;
-        const T *Ks = smem + stage * C::kStage;
-        const T *Vts = Ks + C::kKElems;
+        const float *Ks = smem + stage * C::kStage;
+        const float *Vts = Ks + C::kKElems;
         const int k0 = band.block(t) * kBK;
         const bool has_next = (t + 1 < ntiles);
         if (has_next) ld.load(K, V, band.block(t + 1) * kBK, n, tid);
 
-        // ---- S^T = K Q^T for the two 32-key sub-blocks ----
         f32x16 s[2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
-            if constexpr (BF16) {
-                const T *krow = Ks + (32 * sb + lr) * C::kKStride + 8 * lh;
+            const float *krow = Ks + (32 * sb + lr) * C::kKStride + lh;
 #pragma unroll
-                for (int c = 0; c < D / 16; ++c) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(krow + 16 * c);
-                    s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[sb], 0, 0, 0);
-                }
-            } else {
-                const T *krow = Ks + (32 * sb + lr) * C::kKStride + lh;
-#pragma unroll
-                for (int c = 0; c < D / 2; ++c)
-                    s[sb] = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * c], qf[c], s[sb], 0, 0, 0);
-            }
+            for (int c = 0; c < D / 2; ++c)
+                s[sb] = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * c], qf[c], s[sb], 0, 0, 0);
         }
-        // s[sb][r] = q_qi . k_j with j = k0 + 32 sb + 8 (r/4) + 4 lh + r%4
+        if constexpr (MASKED) mask_tile(s, qi, k0, lh, n, w, g, bias_raw);
+        update_max(s, m_run, negm, l_run, oacc, c2, tau);
 
-        // ---- exact masking (and sink bias) on tiles the band or sinks cut ----
-        if constexpr (MASKED) {
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int j = k0 + 32 * sb + 8 * (r >> 2) + 4 * lh + (r & 3);
-                    const float x = s[sb][r] + (j < g ? bias_raw : 0.f);
-                    s[sb][r] = pair_attended(qi, j, n, w, g) ? x : kNegInf;
-                }
-        }
-
-        // ---- online softmax with a lazily moved reference max ----
-        float mx = kNegInf;
+        float lsum = 0.f;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
-        mx = half_swap_max(mx);
-        if (__any(mx > m_run + tau)) {
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_run - m_new) * c2);
-            m_run = m_new;
-            negm = (m_new == kNegInf) ? 0.f : -m_new * c2;
-            l_run *= alpha;
-#pragma unroll
-            for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
-        }
-
-        // ---- P = exp2(s c2 - m c2); O^T += V^T P^T ----
-        if constexpr (BF16) {
-            bf16x8 pb[4];
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    pb[kc][e] = static_cast<__bf16>(fast_exp2(fmaf(s[kc >> 1][8 * (kc & 1) + e], c2, negm)));
-            // row sum of the bf16 probabilities the value product uses
-            const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
-            float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) {
-                const bf16x2 p01 = {pb[kc][0], pb[kc][1]}, p23 = {pb[kc][2], pb[kc][3]};
-                const bf16x2 p45 = {pb[kc][4], pb[kc][5]}, p67 = {pb[kc][6], pb[kc][7]};
-                ls0 = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, ls0, false);
-                ls1 = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, ls1, false);
-                ls0 = __builtin_amdgcn_fdot2_f32_bf16(p45, ones, ls0, false);
-                ls1 = __builtin_amdgcn_fdot2_f32_bf16(p67, ones, ls1, false);
+            for (int r = 0; r < 16; ++r) {
+                s[sb][r] = fast_exp2(fmaf(s[sb][r], c2, negm));
+                lsum += s[sb][r];
             }
-            l_run += ls0 + ls1;
+        l_run += lsum;
 #pragma unroll
-            for (int cb = 0; cb < D / 32; ++cb) {
-                const T *vrow = Vts + (32 * cb + lr) * C::kVStride + 4 * lh;
-#pragma unroll
-                for (int kc = 0; kc < 4; ++kc) {
-                    const uint2 lo = *reinterpret_cast<const uint2 *>(vrow + 16 * kc);
-                    const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 16 * kc + 8);
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-                    oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc], oacc[cb], 0, 0, 0);
-                }
-            }
-        } else {
-            float lsum = 0.f;
+        for (int cb = 0; cb < D / 32; ++cb) {
+            const float *vrow = Vts + (32 * cb + lr) * C::kVStride + 4 * lh;
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    s[sb][r] = fast_exp2(fmaf(s[sb][r], c2, negm));
-                    lsum += s[sb][r];
-                }
-            l_run += lsum;
-#pragma unroll
-            for (int cb = 0; cb < D / 32; ++cb) {
-                const T *vrow = Vts + (32 * cb + lr) * C::kVStride + 4 * lh;
-#pragma unroll
-                for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float a = vrow[32 * sb + 8 * (r >> 2) + (r & 3)];
-                        oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[sb][r], oacc[cb], 0, 0, 0);
-                    }
-            }
+                for (int r = 0; r < 16; ++r)
+                    oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[32 * sb + 8 * (r >> 2) + (r & 3)], s[sb][r],
+                                                                    oacc[cb], 0, 0, 0);
         }
 
         if (has_next) {
-            T *nxt = smem + (stage ^ 1) * C::kStage;
+            float *nxt = smem + (stage ^ 1) * C::kStage;
             ld.store(nxt, nxt + C::kKElems, tid);
         }
         __syncthreads();
     };
 
-    // Visiting order: sink tiles and the band's lower-edge tiles (masked),
-    // then the run of FULL tiles in a tight loop of its own, then the
-    // diagonal tiles (masked).  The FULL run is contiguous in key-block order.
-    int t_full_lo = ntiles, t_full_hi = ntiles;  // FULL tiles are [t_full_lo, t_full_hi)
-    for (int t = 0; t < ntiles; ++t) {
-        const int kb = band.block(t);
-        if (tile_full(q0, q1, kb * kBK, kb * kBK + kBK - 1, n, w, g)) {
-            if (t_full_lo == ntiles) t_full_lo = t;
-            t_full_hi = t + 1;
-        }
-    }
+    int t_lo, t_hi;
+    full_run(band, q0, q1, n, w, g, &t_lo, &t_hi);
     int t = 0, stage = 0;
-    for (; t < t_full_lo; ++t, stage ^= 1) do_tile(t, stage, std::true_type{});
-    for (; t < t_full_hi; ++t, stage ^= 1) do_tile(t, stage, std::false_type{});
+    for (; t < t_lo; ++t, stage ^= 1) do_tile(t, stage, std::true_type{});
+    for (; t < t_hi; ++t, stage ^= 1) do_tile(t, stage, std::false_type{});
     for (; t < ntiles; ++t, stage ^= 1) do_tile(t, stage, std::true_type{});
 
-    // ---- epilogue: normalise, store O (and LSE) ----
-    const float l_tot = half_swap_sum(l_run);
-    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    if (qi < n) {
-        T *O = reinterpret_cast<T *>(op) + base + (size_t)qi * D;
-#pragma unroll
-        for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int c = 32 * cb + 8 * gq + 4 * lh;
-                const float x0 = oacc[cb][4 * gq + 0] * inv, x1 = oacc[cb][4 * gq + 1] * inv;
-                const float x2 = oacc[cb][4 * gq + 2] * inv, x3 = oacc[cb][4 * gq + 3] * inv;
-                if constexpr (BF16) {
-                    *reinterpret_cast<uint2 *>(O + c) = make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
-                } else {
-                    *reinterpret_cast<float4 *>(O + c) = make_float4(x0, x1, x2, x3);
-                }
-            }
-        if (lsep != nullptr && lh == 0) lsep[(size_t)unit * n + qi] = m_run * scale + logf(l_tot);
-    }
+    store_rows<float, D>(oacc, m_run, l_run, qi, n, lh, op + base, lsep ? lsep + (size_t)unit * n : nullptr, scale);
 }
 
+// ---------------------------------------------------------------------------
 // Host launcher (validated arguments only).
-template <bool BF16, int D>
-static hipError_t launch_prefill_t(const void *q, const void *k, const void *v, void *o, float *lse,
-                                   int units, int n, int w, int g, float scale, float sink_bias,
-                                   hipStream_t stream) {
+hipError_t launch_prefill(const void *q, const void *k, const void *v, void *o, float *lse, int units, int n, int d,
+                          int w, int g, float scale, float sink_bias, bool bf16, hipStream_t stream) {
     const int nqb = (n + kBQ - 1) / kBQ;
     const int total = units * nqb;
     const float c2 = (float)((double)scale * kLog2e);
     const float bias_raw = (float)((double)sink_bias / (double)scale);
-    hipLaunchKernelGGL((prefill_kernel<BF16, D>), dim3(total), dim3(kThreads), 0, stream, q, k, v, o, lse, n,
-                       nqb, w, g, c2, scale, bias_raw, total);
-    return hipGetLastError();
-}
-
-hipError_t launch_prefill(const void *q, const void *k, const void *v, void *o, float *lse, int units,
-                          int n, int d, int w, int g, float scale, float sink_bias, bool bf16,
-                          hipStream_t stream) {
+    const dim3 grid(total), block(kThreads);
     if (bf16) {
-        if (d == 128) return launch_prefill_t<true, 128>(q, k, v, o, lse, units, n, w, g, scale, sink_bias, stream);
-        return launch_prefill_t<true, 64>(q, k, v, o, lse, units, n, w, g, scale, sink_bias, stream);
+        const uint16_t *qq = (const uint16_t *)q, *kk = (const uint16_t *)k, *vv = (const uint16_t *)v;
+        uint16_t *oo = (uint16_t *)o;
+        if (d == 128)
+            hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, block, 0, stream, qq, kk, vv, oo, lse, n, nqb, w, g,
+                               c2, scale, bias_raw, total);
+        else
+            hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, block, 0, stream, qq, kk, vv, oo, lse, n, nqb, w, g,
+                               c2, scale, bias_raw, total);
+    } else {
+        const float *qq = (const float *)q, *kk = (const float *)k, *vv = (const float *)v;
+        float *oo = (float *)o;
+        if (d == 128)
+            hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, block, 0, stream, qq, kk, vv, oo, lse, n, nqb, w, g, c2,
+                               scale, bias_raw, total);
+        else
+            hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, block, 0, stream, qq, kk, vv, oo, lse, n, nqb, w, g, c2,
+                               scale, bias_raw, total);
     }
-    if (d == 128) return launch_prefill_t<false, 128>(q, k, v, o, lse, units, n, w, g, scale, sink_bias, stream);
-    return launch_prefill_t<false, 64>(q, k, v, o, lse, units, n, w, g, scale, sink_bias, stream);
+    return hipGetLastError();
 }
 
 }  // namespace swa
