@@ -18,9 +18,10 @@ hipError_t launch_decode(const void *q, const void *kc, const void *vc, const in
 hipError_t launch_kv_append(void *kc, void *vc, const void *kn, const void *vn, const int64_t *pos, int batch,
                             int heads, int tn, int d, int w, int g, bool bf16, hipStream_t stream);
 size_t decode_workspace_bytes(int units, int d, int rows);
-// prefill tile shape (prefill.hip): 128 query rows x 64 keys for every dtype and d
-constexpr int kPrefillBQ = 128;
+int prefill_rows_per_workgroup(bool bf16);
+// keys per prefill tile (prefill.hip)
 constexpr int kPrefillBK = 64;
+inline int prefill_bq(bool bf16) { return prefill_rows_per_workgroup(bf16); }
 }  // namespace swa
 
 namespace {
@@ -59,9 +60,10 @@ int swa_prefill_fwd(const void *q, const void *k, const void *v, void *o, float 
     if (!std::isfinite(scale) || !(scale > 0.f) || !std::isfinite(sink_bias)) return SWA_EINVAL;
     int st = check_dtype_d(dtype, d);
     if (st != SWA_OK) return st;
-    if (n > INT_MAX - swa::kPrefillBQ) return SWA_EINVAL;
+    const int bq = swa::prefill_bq(dtype == SWA_BF16);
+    if (n > INT_MAX - bq) return SWA_EINVAL;
     const long long units = (long long)batch * heads;
-    const long long nqb = (n + swa::kPrefillBQ - 1) / swa::kPrefillBQ;
+    const long long nqb = (n + bq - 1) / bq;
     if (units * nqb > INT_MAX) return SWA_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned4(lse)))
         return SWA_EALIGN;
@@ -139,7 +141,7 @@ int swa_prefill_tile_shape(swa_dtype_t dtype, int d, int *bq, int *bk) {
     int st = check_dtype_d(dtype, d);
     if (st != SWA_OK) return st;
     if (!bq || !bk) return SWA_EINVAL;
-    *bq = swa::kPrefillBQ;
+    *bq = swa::prefill_bq(dtype == SWA_BF16);
     *bk = swa::kPrefillBK;
     return SWA_OK;
 }

@@ -50,9 +50,10 @@
 
 namespace swa {
 
-constexpr int kBQ = 128;      // query rows per workgroup (4 waves x 32)
-constexpr int kBK = 64;       // keys per tile (2 MFMA sub-blocks of 32)
-constexpr int kThreads = 256;
+constexpr int kBK = 64;        // keys per tile (2 MFMA sub-blocks of 32)
+constexpr int kBQ = 128;       // fp32 path: query rows per workgroup (4 waves x 32)
+constexpr int kThreads = 256;  // fp32 path: threads per workgroup
+constexpr int kWaves16 = 4;    // bf16 path: waves per workgroup (4 x 32 = 128 query rows)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define SWA_LDS __attribute__((address_space(3)))
@@ -70,9 +71,23 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t *p) {
 // Pieces shared by both paths.  s[sb][r] holds q_qi . k_j for the key
 // j = k0 + 32 sb + 8 (r/4) + 4 lh + r%4 (the 32x32 MFMA result layout).
 
-// Exact predicate with sink bias on a cut tile.
+// Exact predicate on a cut tile.  A tile whose keys are all >= g and < n is
+// cut only by the window and causality: 0 <= qi - j < w, one unsigned compare
+// per score.  Tiles with sink keys or past the end of the sequence take the
+// full predicate and the sink bias.
 __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int qi, int k0, int lh, int n, int w, int g,
                                           float bias_raw) {
+    if (k0 >= g && k0 + kBK <= n) {
+        const int diff = qi - k0 - 4 * lh;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int dd = diff - (32 * sb + 8 * (r >> 2) + (r & 3));
+                s[sb][r] = ((unsigned)dd < (unsigned)w) ? s[sb][r] : kNegInf;
+            }
+        return;
+    }
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
@@ -148,13 +163,13 @@ __device__ __forceinline__ void full_run(const BandRange &band, int q0, int q1, 
 
 // ---------------------------------------------------------------------------
 // bf16 path.
-template <int D>
+template <int D, int WAVES>
 struct Bf16Tile {
     static constexpr int kRowBytes = D * 2;
-    static constexpr int kTileBytes = kBK * kRowBytes;         // one K or V tile
-    static constexpr int kStageBytes = 2 * kTileBytes;         // K then V
-    static constexpr int kDmaPerWave = kTileBytes / 1024 / 4;  // 1 KB DMA loads per wave per tile
-    static_assert(kTileBytes % 4096 == 0, "tile split over 4 waves");
+    static constexpr int kTileBytes = kBK * kRowBytes;             // one K or V tile
+    static constexpr int kStageBytes = 2 * kTileBytes;             // K then V
+    static constexpr int kDmaPerWave = kTileBytes / 1024 / WAVES;  // 1 KB DMA loads per wave per tile
+    static_assert(kTileBytes % (1024 * WAVES) == 0, "tile split over the waves");
     // LDS byte offset of K(key, 16-byte chunk c): 64-byte column block c/4,
     // 64 bytes per key inside it, chunk position (c%4) ^ ((key/4)%4).
     __device__ static constexpr uint32_t k_off(int key, int c) {
@@ -166,12 +181,13 @@ struct Bf16Tile {
     }
 };
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
+template <int D, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp, const uint16_t *__restrict__ vp,
     uint16_t *__restrict__ op, float *__restrict__ lsep, int n, int nqb, int w, int g, float c2, float scale,
     float bias_raw, int total_wg) {
-    using L = Bf16Tile<D>;
+    using L = Bf16Tile<D, WAVES>;
+    constexpr int BQ = 32 * WAVES;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * L::kStageBytes];
 
     const int tid = threadIdx.x;
@@ -187,8 +203,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const uint16_t *K = kp + base;
     const uint16_t *V = vp + base;
 
-    const int q0 = qb * kBQ;
-    const int q1 = min(q0 + kBQ, n) - 1;
+    const int q0 = qb * BQ;
+    const int q1 = min(q0 + BQ, n) - 1;
     const int qi = q0 + wave * 32 + lr;
     const BandRange band = band_range(q0, q1, w, g, kBK);
     const int ntiles = band.count();
@@ -204,11 +220,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
             qf[c] = __builtin_bit_cast(bf16x8, buffer_load16(rq, rowoff + (16 * c + 8 * lh) * 2));
     }
 
-    // ---- DMA of one K/V tile into a stage: each wave moves its share ----
-    // DMA load i of this wave fills LDS bytes [1 KB m, 1 KB (m+1)) of the tile,
-    // m = wave * kDmaPerWave + i: column block m/4, keys 16 (m%4) + lane/4,
-    // chunk position lane%4.  The global chunk that belongs there undoes the
-    // swizzle (K) or is the same chunk (V).
+    // ---- DMA of K and V tiles into LDS: each wave moves its share ----
+    // LDS holds two K buffers and two V buffers.  DMA load i of this wave
+    // fills bytes [1 KB m, 1 KB (m+1)) of a tile, m = wave * kDmaPerWave + i:
+    // column block m/4, keys 16 (m%4) + lane/4, chunk position lane%4.  The
+    // global chunk that belongs there undoes the swizzle (K) or is the same
+    // chunk (V).
     uint32_t dma_k[L::kDmaPerWave], dma_v[L::kDmaPerWave];
 #pragma unroll
     for (int i = 0; i < L::kDmaPerWave; ++i) {
@@ -220,20 +237,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
         dma_k[i] = key * L::kRowBytes + 16 * ck;
         dma_v[i] = key * L::kRowBytes + 16 * cv;
     }
-    auto dma_tile = [&](int k0, int stage) {
-        const uint32_t bytes = (uint32_t)(n - k0) * L::kRowBytes;
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + (size_t)k0 * D, bytes);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + (size_t)k0 * D, bytes);
+    uint8_t *const kbuf = smem;                       // K buffers 0, 1
+    uint8_t *const vbuf = smem + 2 * L::kTileBytes;   // V buffers 0, 1
+    auto dma = [&](const uint16_t *src, const uint32_t *offs, int k0, uint8_t *dst) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)k0 * D, (uint32_t)(n - k0) * L::kRowBytes);
 #pragma unroll
-        for (int i = 0; i < L::kDmaPerWave; ++i) {
-            const int m = wave * L::kDmaPerWave + i;
-            uint8_t *dk = smem + stage * L::kStageBytes + m * 1024;
-            dma16(rk, dk, dma_k[i]);
-            dma16(rv, dk + L::kTileBytes, dma_v[i]);
-        }
+        for (int i = 0; i < L::kDmaPerWave; ++i) dma16(r, dst + (wave * L::kDmaPerWave + i) * 1024, offs[i]);
     };
 
-    // Per-lane LDS read offsets within a stage.
+    // Per-lane LDS read offsets within a buffer.
     // K operand: row 32 sb + lr, 16-byte chunk 2c + lh; even and odd c differ
     // in the chunk position, c/2 selects the column block.
     const uint32_t koff_even = L::k_off(lr, lh);
@@ -243,7 +255,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     // columns 16 (G%2) + 4 (j%4) .. +3; the instruction hands lane j of the
     // group column 16 (G%2) + j of four consecutive keys.
     const int grp = lane >> 4, jj = lane & 15;
-    const uint32_t voff = (uint32_t)L::kTileBytes + L::v_off(4 * (grp >> 1) + (jj >> 2), 4 * (grp & 1) + (jj & 3));
+    const uint32_t voff = L::v_off(4 * (grp >> 1) + (jj >> 2), 4 * (grp & 1) + (jj & 3));
+
+    // S^T = K Q^T of one tile whose K sits at kb
+    auto scores = [&](const uint8_t *kb, f32x16 (&s)[2]) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) {
+                const uint32_t off = ((c & 1) ? koff_odd : koff_even) + (c >> 1) * (kBK * 64) + sb * 32 * 64;
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kb + off);
+                s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[sb], 0, 0, 0);
+            }
+        }
+    };
 
     f32x16 oacc[D / 32];
 #pragma unroll
@@ -252,31 +279,34 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
         for (int r = 0; r < 16; ++r) oacc[cb][r] = 0.f;
     float m_run = kNegInf, negm = 0.f, l_run = 0.f;
 
-    dma_tile(band.block(0) * kBK, 0);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA has landed
+    // Pipeline: while the softmax of tile t runs on the VALU, the matrix core
+    // computes the scores of tile t+1.  During tile t the DMA fills K(t+2) into
+    // the K buffer that K(t) left and V(t+1) into the V buffer that V(t-1)
+    // left, so every DMA has a whole tile of time to land.
+    dma(K, dma_k, band.block(0) * kBK, kbuf);
+    dma(V, dma_v, band.block(0) * kBK, vbuf);
+    if (ntiles > 1) dma(K, dma_k, band.block(1) * kBK, kbuf + L::kTileBytes);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    f32x16 s_cur[2];
+    scores(kbuf, s_cur);
+    __syncthreads();  // every wave is done with K(0) before K(2) replaces it
 
-    auto do_tile = [&](int t, int stage, auto masked_tag) {
+    auto do_tile = [&](int t, auto masked_tag) {
         constexpr bool MASKED = decltype(masked_tag)::value;
-        const uint8_t *sbase = smem + stage * L::kStageBytes;
+        const int cur = t & 1, nxt = cur ^ 1;
         const int k0 = band.block(t) * kBK;
-        if (t + 1 < ntiles) dma_tile(band.block(t + 1) * kBK, stage ^ 1);
+        if (t + 2 < ntiles) dma(K, dma_k, band.block(t + 2) * kBK, kbuf + cur * L::kTileBytes);
+        if (t + 1 < ntiles) dma(V, dma_v, band.block(t + 1) * kBK, vbuf + nxt * L::kTileBytes);
 
-        // ---- S^T = K Q^T ----
-        f32x16 s[2];
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
-#pragma unroll
-            for (int c = 0; c < D / 16; ++c) {
-                const uint32_t off = ((c & 1) ? koff_odd : koff_even) + (c >> 1) * (kBK * 64) + sb * 32 * 64;
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sbase + off);
-                s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[sb], 0, 0, 0);
-            }
-        }
-        if constexpr (MASKED) mask_tile(s, qi, k0, lh, n, w, g, bias_raw);
-        update_max(s, m_run, negm, l_run, oacc, c2, tau);
+        if constexpr (MASKED) mask_tile(s_cur, qi, k0, lh, n, w, g, bias_raw);
+        update_max(s_cur, m_run, negm, l_run, oacc, c2, tau);
+
+        // Scores of the next tile, issued here so that they share one block
+        // with the exponentials below and the two interleave (on the last
+        // tile this reads the other K buffer and the result is discarded).
+        f32x16 s_nxt[2];
+        scores(kbuf + nxt * L::kTileBytes, s_nxt);
 
         // ---- P = exp2(s c2 - m c2), row sum, O^T += V^T P^T ----
         bf16x8 pb[4];
@@ -284,7 +314,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
         for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                pb[kc][e] = static_cast<__bf16>(fast_exp2(fmaf(s[kc >> 1][8 * (kc & 1) + e], c2, negm)));
+                pb[kc][e] = static_cast<__bf16>(fast_exp2(fmaf(s_cur[kc >> 1][8 * (kc & 1) + e], c2, negm)));
         const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
         float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
@@ -297,28 +327,34 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
             ls1 = __builtin_amdgcn_fdot2_f32_bf16(p67, ones, ls1, false);
         }
         l_run += ls0 + ls1;
+        const uint8_t *vb = vbuf + cur * L::kTileBytes + voff;
 #pragma unroll
         for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc) {
                 // keys 16 kc + 4 lh + 0..3 (first read) and 16 kc + 8 + 4 lh + 0..3
-                const uint8_t *p0 = sbase + voff + cb * (kBK * 64) + (16 * kc) * 64;
+                const uint8_t *p0 = vb + cb * (kBK * 64) + (16 * kc) * 64;
                 const s16x4 lo = lds_read_tr16(p0);
                 const s16x4 hi = lds_read_tr16(p0 + 8 * 64);
                 const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc], oacc[cb], 0, 0, 0);
             }
+        s_cur[0] = s_nxt[0];
+        s_cur[1] = s_nxt[1];
 
-        __builtin_amdgcn_s_waitcnt(0);  // the next tile's DMA of this wave has landed
+        __builtin_amdgcn_s_waitcnt(0);  // K(t+2) and V(t+1) of this wave have landed
         __syncthreads();
     };
 
-    int t_lo, t_hi;
-    full_run(band, q0, q1, n, w, g, &t_lo, &t_hi);
-    int t = 0, stage = 0;
-    for (; t < t_lo; ++t, stage ^= 1) do_tile(t, stage, std::true_type{});
-    for (; t < t_hi; ++t, stage ^= 1) do_tile(t, stage, std::false_type{});
-    for (; t < ntiles; ++t, stage ^= 1) do_tile(t, stage, std::true_type{});
+    // FULL tiles for this wave's own 32 rows: the band edges of the
+    // workgroup's block cut a single wave's rows in fewer tiles.
+    int t_lo = 0, t_hi = ntiles;  // a wave entirely past n keeps all tiles unmasked (nothing is stored)
+    const int qw0 = q0 + wave * 32;
+    if (qw0 < n) full_run(band, qw0, min(qw0 + 31, n - 1), n, w, g, &t_lo, &t_hi);
+    int t = 0;
+    for (; t < t_lo; ++t) do_tile(t, std::true_type{});
+    for (; t < t_hi; ++t) do_tile(t, std::false_type{});
+    for (; t < ntiles; ++t) do_tile(t, std::true_type{});
 
     store_rows<uint16_t, D>(oacc, m_run, l_run, qi, n, lh, op + base, lsep ? lsep + (size_t)unit * n : nullptr,
                             scale);
@@ -498,24 +534,31 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Query rows per workgroup (the prefill grid is units x ceil(n / rows)).
+int prefill_rows_per_workgroup(bool bf16) { return bf16 ? 32 * kWaves16 : kBQ; }
+
 // Host launcher (validated arguments only).
 hipError_t launch_prefill(const void *q, const void *k, const void *v, void *o, float *lse, int units, int n, int d,
                           int w, int g, float scale, float sink_bias, bool bf16, hipStream_t stream) {
-    const int nqb = (n + kBQ - 1) / kBQ;
-    const int total = units * nqb;
     const float c2 = (float)((double)scale * kLog2e);
     const float bias_raw = (float)((double)sink_bias / (double)scale);
-    const dim3 grid(total), block(kThreads);
     if (bf16) {
+        const int bq = 32 * kWaves16;
+        const int nqb = (n + bq - 1) / bq;
+        const int total = units * nqb;
+        const dim3 grid(total), block(64 * kWaves16);
         const uint16_t *qq = (const uint16_t *)q, *kk = (const uint16_t *)k, *vv = (const uint16_t *)v;
         uint16_t *oo = (uint16_t *)o;
         if (d == 128)
-            hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, block, 0, stream, qq, kk, vv, oo, lse, n, nqb, w, g,
-                               c2, scale, bias_raw, total);
+            hipLaunchKernelGGL((prefill_bf16_kernel<128, kWaves16>), grid, block, 0, stream, qq, kk, vv, oo, lse, n,
+                               nqb, w, g, c2, scale, bias_raw, total);
         else
-            hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, block, 0, stream, qq, kk, vv, oo, lse, n, nqb, w, g,
-                               c2, scale, bias_raw, total);
+            hipLaunchKernelGGL((prefill_bf16_kernel<64, kWaves16>), grid, block, 0, stream, qq, kk, vv, oo, lse, n,
+                               nqb, w, g, c2, scale, bias_raw, total);
     } else {
+        const int nqb = (n + kBQ - 1) / kBQ;
+        const int total = units * nqb;
+        const dim3 grid(total), block(kThreads);
         const float *qq = (const float *)q, *kk = (const float *)k, *vv = (const float *)v;
         float *oo = (float *)o;
         if (d == 128)

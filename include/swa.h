@@ -129,8 +129,10 @@ const char *swa_strerror(int status);
  * prefill kernel visits when queries are grouped bq at a time and keys bk at
  * a time, in visiting order, query block by query block.  is_full = 1 means
  * every pair of the tile with query < n is attended and carries no sink bias,
- * so the kernel skips masking there.  Returns the number of triples (writing
- * at most `cap`), or a negative status.
+ * so masking can be skipped there.  The kernel visits the tiles of its
+ * workgroup's query block (bq from swa_prefill_tile_shape) and applies the
+ * is_full test to each wave's own 32 query rows.  Returns the number of
+ * triples (writing at most `cap`), or a negative status.
  */
 long swa_band_tiles(int n, int w, int g, int bq, int bk, int *out, long cap);
 

@@ -44,15 +44,15 @@ def _check(orc, n, w, g, bq, bk):
 
 
 @pytest.mark.parametrize("n,w,g", SHAPES)
-@pytest.mark.parametrize("bq,bk", TILES)
+@pytest.mark.parametrize("bq,bk", TILES + [(256, 64), (32, 64)])
 def test_schedule_cover_minimal_full(orc, n, w, g, bq, bk):
     _check(orc, n, w, g, bq, bk)
 
 
 def test_kernel_tile_shape():
-    for dt in (swa.SWA_F32, swa.SWA_BF16):
-        for d in (64, 128):
-            assert swa.prefill_tile_shape(dt, d) == (128, 64)
+    for d in (64, 128):
+        assert swa.prefill_tile_shape(swa.SWA_BF16, d) == (128, 64)
+        assert swa.prefill_tile_shape(swa.SWA_F32, d) == (128, 64)
 
 
 def _count_closed_form(n, w, g, bq, bk):
