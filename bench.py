@@ -46,10 +46,31 @@ DECODE = {
     "rolling_decode": (64, 32, 128, 4096, 4, 4096, 131072, 4),
 }
 
-# Traffic measured with rocprofv3 counters (FETCH_SIZE + WRITE_SIZE per
-# dispatch, scaled by the copy-kernel calibration); None until measured for
-# the kernel as it stands.
-MEASURED_TRAFFIC_BYTES = {}
+# HBM traffic per launch measured with rocprofv3 counters (FETCH_SIZE and
+# WRITE_SIZE per dispatch, each scaled by what the same counter reads for a
+# plain device copy of known size, see --calibrate-copy), keyed by workload.
+# Each entry records a digest of the kernel source it was measured on; when
+# the source has changed since, the figure no longer describes the kernel and
+# `traffic` is reported as null.
+MEASURED_TRAFFIC = {}
+CSRC = os.path.join(ROOT, "block_sparse_causal_band_amd", "csrc")
+
+
+def kernel_source_digest(name: str) -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in ("common.h", "schedule.h", name):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, source: str):
+    entry = MEASURED_TRAFFIC.get(workload)
+    if entry is None or entry["source_digest"] != kernel_source_digest(source):
+        return None
+    return entry["bytes"]
 
 
 def row_pairs(i: int, w: int, g: int) -> int:
@@ -112,7 +133,7 @@ def bench_prefill(name, steps, warmup):
     flops = 4.0 * d * band_pairs(n, w, g) * B * H
     peak = PEAK_BF16_TFLOPS if dtype == torch.bfloat16 else PEAK_F32_TFLOPS
     achieved = flops / (ms_launch * 1e-3) / 1e12
-    traffic = MEASURED_TRAFFIC_BYTES.get(name)
+    traffic = measured_traffic(name, "prefill.hip")
     return {
         "ms_per_step": ms_step,
         "value": flops / (ms_step * 1e-3) / 1e12,
@@ -123,7 +144,7 @@ def bench_prefill(name, steps, warmup):
                    "page_formula_flops_4nwd": 4.0 * n * w * d * B * H},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
-                     "kernel": f"prefill_kernel<{'bf16' if dtype == torch.bfloat16 else 'f32'},{d}>",
+                     "kernel": f"prefill_bf16_kernel<{d},4>" if dtype == torch.bfloat16 else f"prefill_f32_kernel<{d}>",
                      "avg_launch_ms": ms_launch, "min_launch_ms": min(per)},
     }
 
@@ -153,7 +174,7 @@ def bench_decode(name, steps, warmup):
     rows = sum(row_pairs(int(p), w, g) for p in pos.cpu().tolist()) * H
     nbytes = rows * d * 2 * 2 + 2 * B * H * d * 2
     achieved = nbytes / (ms_launch * 1e-3) / 1e9
-    traffic = MEASURED_TRAFFIC_BYTES.get(name)
+    traffic = measured_traffic(name, "decode.hip")
     return {
         "ms_per_step": ms_step,
         "value": nbytes / (ms_step * 1e-3) / 1e9,
@@ -240,6 +261,27 @@ def cpu_baseline_decode(name, budget_s=10.0):
             "sample": f"{done} (batch, head) queries of {name}, fp64, {dt:.1f} s"}
 
 
+def calibrate_copy(steps: int, nbytes: int = 1 << 30):
+    """A plain device-to-device copy of known size, for scaling the HBM
+    byte counters: FETCH_SIZE and WRITE_SIZE of these dispatches should each
+    read nbytes."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": nbytes, "bytes_written_per_copy": nbytes,
+                      "copies": steps, "ms_per_copy": dt * 1e3, "GB_per_s_read_plus_write": 2 * nbytes / dt / 1e9}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -248,6 +290,8 @@ def main():
     ap.add_argument("--workload", default="mistral_prefill", choices=sorted(PREFILL) + sorted(DECODE))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode figures on a prefill line")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -259,6 +303,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy(args.steps)
+        return
 
     if args.workload in PREFILL:
         r = bench_prefill(args.workload, args.steps, args.warmup)

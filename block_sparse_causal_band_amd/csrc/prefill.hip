@@ -305,7 +305,11 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
         // Scores of the next tile, issued here so that they share one block
         // with the exponentials below and the two interleave (on the last
         // tile this reads the other K buffer and the result is discarded).
+        // The matrix-heavy stretch of the tile runs at raised wave priority:
+        // when both waves of a SIMD are ready, the one feeding the matrix core
+        // issues first and the other's VALU work fills the gaps.
         f32x16 s_nxt[2];
+        __builtin_amdgcn_s_setprio(1);
         scores(kbuf + nxt * L::kTileBytes, s_nxt);
 
         // ---- P = exp2(s c2 - m c2), row sum, O^T += V^T P^T ----
@@ -341,6 +345,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
             }
         s_cur[0] = s_nxt[0];
         s_cur[1] = s_nxt[1];
+        __builtin_amdgcn_s_setprio(0);
 
         __builtin_amdgcn_s_waitcnt(0);  // K(t+2) and V(t+1) of this wave have landed
         __syncthreads();
