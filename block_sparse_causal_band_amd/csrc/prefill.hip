@@ -302,47 +302,89 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
         if constexpr (MASKED) mask_tile(s_cur, qi, k0, lh, n, w, g, bias_raw);
         update_max(s_cur, m_run, negm, l_run, oacc, c2, tau);
 
-        // Scores of the next tile, issued here so that they share one block
-        // with the exponentials below and the two interleave (on the last
-        // tile this reads the other K buffer and the result is discarded).
-        // The matrix-heavy stretch of the tile runs at raised wave priority:
-        // when both waves of a SIMD are ready, the one feeding the matrix core
-        // issues first and the other's VALU work fills the gaps.
-        f32x16 s_nxt[2];
-        __builtin_amdgcn_s_setprio(1);
-        scores(kbuf + nxt * L::kTileBytes, s_nxt);
+        // The rest of the tile is two interleaved streams, in a fixed order
+        // (sched_barrier pins it; the compiler would otherwise group like
+        // with like, and long runs of MFMAs with no VALU work between them
+        // leave the matrix core and the VALU taking turns):
+        //  A: the score MFMAs of tile t+1, each followed by the exponentials
+        //     of 32/NS scores of tile t (K fragments read 4 MFMAs ahead);
+        //  B: the PV MFMAs of tile t, each group of them preceded by the
+        //     bf16 packing and row-sum dot2s of its probabilities (V^T
+        //     fragments read 3 MFMAs ahead).
+        // On the last tile the A stream reads the other K buffer and its
+        // result is discarded.  The whole stretch runs at raised wave
+        // priority, so when both waves of a SIMD are ready the one feeding
+        // the matrix core issues first.
+        const uint8_t *kb = kbuf + nxt * L::kTileBytes;
+        const uint8_t *vb = vbuf + cur * L::kTileBytes + voff;
+        constexpr int NC = D / 16;       // MFMAs per 32-key score sub-block
+        constexpr int NS = 2 * NC;       // score MFMAs per tile
+        constexpr int EPS = 32 / NS;     // exponentials per score MFMA
+        constexpr int NP = 4 * (D / 32); // PV MFMAs per tile
+        constexpr int KA = 4, VA = 3;    // read-ahead depths
+        auto kfrag = [&](int j) -> bf16x8 {
+            const int sb = j / NC, c = j % NC;
+            const uint32_t off = ((c & 1) ? koff_odd : koff_even) + (c >> 1) * (kBK * 64) + sb * 32 * 64;
+            return *reinterpret_cast<const bf16x8 *>(kb + off);
+        };
+        auto vfrag = [&](int j) -> bf16x8 {  // j = kc * (D/32) + cb
+            const int kc = j / (D / 32), cb = j % (D / 32);
+            // keys 16 kc + 4 lh + 0..3 (first read) and 16 kc + 8 + 4 lh + 0..3
+            const uint8_t *p0 = vb + cb * (kBK * 64) + (16 * kc) * 64;
+            const s16x4 lo = lds_read_tr16(p0);
+            const s16x4 hi = lds_read_tr16(p0 + 8 * 64);
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
 
-        // ---- P = exp2(s c2 - m c2), row sum, O^T += V^T P^T ----
-        bf16x8 pb[4];
+        __builtin_amdgcn_s_setprio(1);
+        f32x16 s_nxt[2];
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
+        for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                pb[kc][e] = static_cast<__bf16>(fast_exp2(fmaf(s_cur[kc >> 1][8 * (kc & 1) + e], c2, negm)));
+            for (int r = 0; r < 16; ++r) s_nxt[sb][r] = 0.f;
+        bf16x8 kf[KA];
+#pragma unroll
+        for (int j = 0; j < KA; ++j) kf[j] = kfrag(j);
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            const bf16x8 a = kf[j % KA];
+            if (j + KA < NS) kf[j % KA] = kfrag(j + KA);
+            s_nxt[j / NC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[j % NC], s_nxt[j / NC], 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < EPS; ++q) {
+                const int e = EPS * j + q;
+                s_cur[e >> 4][e & 15] = fast_exp2(fmaf(s_cur[e >> 4][e & 15], c2, negm));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        bf16x8 vf[VA];
+#pragma unroll
+        for (int j = 0; j < VA; ++j) vf[j] = vfrag(j);
         const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
         float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
-            const bf16x2 p01 = {pb[kc][0], pb[kc][1]}, p23 = {pb[kc][2], pb[kc][3]};
-            const bf16x2 p45 = {pb[kc][4], pb[kc][5]}, p67 = {pb[kc][6], pb[kc][7]};
+            // probabilities of keys 16 kc + {4 lh + 0..3, 8 + 4 lh + 0..3}, rounded to bf16
+            bf16x8 pk;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pk[e] = static_cast<__bf16>(s_cur[kc >> 1][8 * (kc & 1) + e]);
+            const bf16x2 p01 = {pk[0], pk[1]}, p23 = {pk[2], pk[3]};
+            const bf16x2 p45 = {pk[4], pk[5]}, p67 = {pk[6], pk[7]};
             ls0 = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, ls0, false);
             ls1 = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, ls1, false);
             ls0 = __builtin_amdgcn_fdot2_f32_bf16(p45, ones, ls0, false);
             ls1 = __builtin_amdgcn_fdot2_f32_bf16(p67, ones, ls1, false);
+#pragma unroll
+            for (int cb = 0; cb < D / 32; ++cb) {
+                const int j = kc * (D / 32) + cb;
+                const bf16x8 a = vf[j % VA];
+                if (j + VA < NP) vf[j % VA] = vfrag(j + VA);
+                oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk, oacc[cb], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         l_run += ls0 + ls1;
-        const uint8_t *vb = vbuf + cur * L::kTileBytes + voff;
-#pragma unroll
-        for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) {
-                // keys 16 kc + 4 lh + 0..3 (first read) and 16 kc + 8 + 4 lh + 0..3
-                const uint8_t *p0 = vb + cb * (kBK * 64) + (16 * kc) * 64;
-                const s16x4 lo = lds_read_tr16(p0);
-                const s16x4 hi = lds_read_tr16(p0 + 8 * 64);
-                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc], oacc[cb], 0, 0, 0);
-            }
         s_cur[0] = s_nxt[0];
         s_cur[1] = s_nxt[1];
         __builtin_amdgcn_s_setprio(0);
