@@ -123,9 +123,12 @@ long swa_band_tiles(int n, int w, int g, int bq, int bk, int *out, long cap) {
         const int q0 = qb * bq;
         const int q1 = (q0 + bq < n ? q0 + bq : n) - 1;
         const swa::BandRange r = swa::band_range(q0, q1, w, g, bk);
+        int t_lo, t_hi;  // the kernels' closed form; the per-tile test must agree with it
+        swa::full_range(r, q0, q1, n, w, g, bk, &t_lo, &t_hi);
         for (int t = 0; t < r.count(); ++t) {
             const int kb = r.block(t);
             const int full = swa::tile_full(q0, q1, kb * bk, kb * bk + bk - 1, n, w, g) ? 1 : 0;
+            if (full != ((t >= t_lo && t < t_hi) ? 1 : 0)) return SWA_EINVAL;
             if (count < cap) {
                 out[3 * count + 0] = qb;
                 out[3 * count + 1] = kb;

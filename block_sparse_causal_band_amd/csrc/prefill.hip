@@ -146,21 +146,6 @@ __device__ __forceinline__ void store_rows(const f32x16 (&oacc)[D / 32], float m
     if (lse != nullptr && lh == 0) lse[qi] = m_run * scale + logf(l_tot);
 }
 
-// FULL tiles are a contiguous run [t_lo, t_hi) of the visiting order.
-__device__ __forceinline__ void full_run(const BandRange &band, int q0, int q1, int n, int w, int g, int *t_lo,
-                                         int *t_hi) {
-    const int nt = band.count();
-    *t_lo = nt;
-    *t_hi = nt;
-    for (int t = 0; t < nt; ++t) {
-        const int kb = band.block(t);
-        if (tile_full(q0, q1, kb * kBK, kb * kBK + kBK - 1, n, w, g)) {
-            if (*t_lo == nt) *t_lo = t;
-            *t_hi = t + 1;
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
 // bf16 path.
 template <int D, int WAVES>
@@ -397,7 +382,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     // workgroup's block cut a single wave's rows in fewer tiles.
     int t_lo = 0, t_hi = ntiles;  // a wave entirely past n keeps all tiles unmasked (nothing is stored)
     const int qw0 = q0 + wave * 32;
-    if (qw0 < n) full_run(band, qw0, min(qw0 + 31, n - 1), n, w, g, &t_lo, &t_hi);
+    if (qw0 < n) full_range(band, qw0, min(qw0 + 31, n - 1), n, w, g, kBK, &t_lo, &t_hi);
     int t = 0;
     for (; t < t_lo; ++t) do_tile(t, std::true_type{});
     for (; t < t_hi; ++t) do_tile(t, std::false_type{});
@@ -571,7 +556,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
     };
 
     int t_lo, t_hi;
-    full_run(band, q0, q1, n, w, g, &t_lo, &t_hi);
+    full_range(band, q0, q1, n, w, g, kBK, &t_lo, &t_hi);
     int t = 0, stage = 0;
     for (; t < t_lo; ++t, stage ^= 1) do_tile(t, stage, std::true_type{});
     for (; t < t_hi; ++t, stage ^= 1) do_tile(t, stage, std::false_type{});

@@ -74,4 +74,27 @@ __host__ __device__ inline void workgroup_order(int bid, int total, int nqb, int
     *qb = nqb - 1 - (logical % nqb);
 }
 
+// The FULL tiles of query rows [qa, qz] (qz < n) are one contiguous run
+// [*t_lo, *t_hi) of the visiting order of band r (sink blocks, which hold a
+// position < g, are never FULL); an empty run is reported as [count, count).
+// Closed form of the per-tile test tile_full.
+__host__ __device__ inline void full_range(const BandRange &r, int qa, int qz, int n, int w, int g, int bk,
+                                           int *t_lo, int *t_hi) {
+    int lo_key = qz - w + 1;  // smallest key every row of the block attends in the window
+    if (lo_key < g) lo_key = g;
+    if (lo_key < 0) lo_key = 0;
+    int kb_a = (lo_key + bk - 1) / bk;  // first block whose keys are all >= lo_key
+    int kb_b = (qa + 1) / bk - 1;       // last block whose keys are all <= qa
+    const int kb_n = n / bk - 1;        // last block entirely below n
+    if (kb_b > kb_n) kb_b = kb_n;
+    if (kb_a < r.kb_lo) kb_a = r.kb_lo;
+    if (kb_b > r.kb_hi) kb_b = r.kb_hi;
+    if (kb_a > kb_b) {
+        *t_lo = *t_hi = r.count();
+    } else {
+        *t_lo = r.ns + (kb_a - r.kb_lo);
+        *t_hi = r.ns + (kb_b - r.kb_lo) + 1;
+    }
+}
+
 }  // namespace swa

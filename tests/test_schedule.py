@@ -10,7 +10,7 @@ SHAPES = [
     (8, 3, 0), (8, 3, 1), (257, 1, 0), (257, 63, 0), (257, 64, 4), (257, 65, 0), (300, 300, 0),
     (300, 1000, 2), (1000, 127, 65), (1000, 129, 130), (777, 300, 4), (64, 64, 64), (129, 5, 200),
 ]
-TILES = [(128, 64), (64, 64), (32, 32), (128, 128), (16, 48)]
+TILES = [(128, 64), (64, 64), (32, 32), (128, 128), (16, 48), (256, 32)]
 
 
 def _check(orc, n, w, g, bq, bk):
@@ -68,11 +68,11 @@ def _count_closed_form(n, w, g, bq, bk):
 
 
 @pytest.mark.parametrize("n,w,g", [(16384, 4096, 0), (32768, 4096, 4), (131072, 1024, 0)])
-def test_real_config_tile_counts(n, w, g):
-    tiles = swa.band_tiles(n, w, g, 128, 64)
-    assert len(tiles) == _count_closed_form(n, w, g, 128, 64)
-    dense_causal = sum(min(n, (qb + 1) * 128) // 64 + (1 if min(n, (qb + 1) * 128) % 64 else 0)
-                       for qb in range((n + 127) // 128))
+@pytest.mark.parametrize("bq,bk", [(128, 64), (256, 32)])
+def test_real_config_tile_counts(n, w, g, bq, bk):
+    tiles = swa.band_tiles(n, w, g, bq, bk)
+    assert len(tiles) == _count_closed_form(n, w, g, bq, bk)
+    dense_causal = sum(-(-min(n, (qb + 1) * bq) // bk) for qb in range((n + bq - 1) // bq))
     assert len(tiles) < dense_causal
 
 
