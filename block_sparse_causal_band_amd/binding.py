@@ -54,6 +54,14 @@ def lib() -> ctypes.CDLL:
         L.swa_decode_fwd.restype = _int
         L.swa_decode_workspace_bytes.argtypes = [_int] * 5
         L.swa_decode_workspace_bytes.restype = ctypes.c_size_t
+        L.swa_prefill_fwd_gqa.argtypes = [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _int, _int,
+                                          _flt, _flt, _int, _vp]
+        L.swa_prefill_fwd_gqa.restype = _int
+        L.swa_decode_fwd_gqa.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _int,
+                                         _flt, _flt, _int, _vp, ctypes.c_size_t, _vp]
+        L.swa_decode_fwd_gqa.restype = _int
+        L.swa_decode_workspace_bytes_gqa.argtypes = [_int] * 6
+        L.swa_decode_workspace_bytes_gqa.restype = ctypes.c_size_t
         L.swa_strerror.argtypes = [_int]
         L.swa_strerror.restype = ctypes.c_char_p
         L.swa_band_tiles.argtypes = [_int, _int, _int, _int, _int, _vp, ctypes.c_long]
@@ -101,27 +109,33 @@ def _dev_tensor(t, name):
 
 def prefill(q, k, v, w: int, g: int = 0, scale: float | None = None, sink_bias: float = 0.0,
             return_lse: bool = False, out=None):
-    """Causal sliding-window attention with sinks over q, k, v [batch, heads, n, d]."""
+    """Causal sliding-window attention with sinks: q [batch, heads, n, d] against
+    k, v [batch, kv_heads, n, d] (kv_heads == heads: multi-head attention; a
+    divisor of heads: grouped-query attention, query head h reads key/value
+    head h // (heads // kv_heads))."""
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v)):
         _dev_tensor(t, name)
-    _need(q.dim() == 4 and q.shape == k.shape == v.shape, "q, k, v must share one shape [batch, heads, n, d]")
+    _need(q.dim() == 4 and k.dim() == 4 and k.shape == v.shape, "q, k, v must be 4-d, k and v one shape")
+    _need(q.shape[0] == k.shape[0] and q.shape[2:] == k.shape[2:],
+          "q [batch, heads, n, d] and k, v [batch, kv_heads, n, d] must agree on batch, n, d")
     _need(q.dtype == k.dtype == v.dtype, "q, k, v must share one dtype")
     _need(q.device == k.device == v.device, "q, k, v must be on one device")
     B, H, n, d = q.shape
+    Hkv = k.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = torch.empty_like(q) if out is None else out
     _dev_tensor(o, "out")
     _need(o.shape == q.shape and o.dtype == q.dtype and o.device == q.device, "out must match q")
     lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device) if return_lse else None
-    rc = lib().swa_prefill_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                               lse.data_ptr() if lse is not None else None,
-                               B, H, n, d, int(w), int(g), float(scale), float(sink_bias),
-                               _dtype_code(q), _stream(q))
+    rc = lib().swa_prefill_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   lse.data_ptr() if lse is not None else None,
+                                   B, H, Hkv, n, d, int(w), int(g), float(scale), float(sink_bias),
+                                   _dtype_code(q), _stream(q))
     if rc != 0:
-        raise SwaError(rc, "swa_prefill_fwd")
+        raise SwaError(rc, "swa_prefill_fwd_gqa")
     return (o, lse) if return_lse else o
 
 
@@ -145,19 +159,24 @@ def kv_append(k_cache, v_cache, k_new, v_new, pos, w: int, g: int = 0):
         raise SwaError(rc, "swa_kv_append")
 
 
-def decode_workspace_bytes(batch: int, heads: int, d: int, w: int, g: int) -> int:
-    return int(lib().swa_decode_workspace_bytes(batch, heads, d, w, g))
+def decode_workspace_bytes(batch: int, heads: int, d: int, w: int, g: int, kv_heads: int | None = None) -> int:
+    if kv_heads is None:
+        return int(lib().swa_decode_workspace_bytes(batch, heads, d, w, g))
+    return int(lib().swa_decode_workspace_bytes_gqa(batch, heads, kv_heads, d, w, g))
 
 
 def decode(q, k_cache, v_cache, pos, w: int, g: int = 0, scale: float | None = None, sink_bias: float = 0.0,
            return_lse: bool = False, workspace=None, out=None):
-    """One query per (batch, head), q [batch, heads, d], at positions pos [batch]."""
+    """One query per (batch, head), q [batch, heads, d], at positions pos [batch],
+    against caches [batch, kv_heads, g + w, d] (kv_heads divides heads)."""
     import torch
 
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("pos", pos)):
         _dev_tensor(t, name)
     B, H, d = q.shape
-    _need(k_cache.shape == v_cache.shape == (B, H, g + w, d), f"caches must be [batch, heads, g + w, d]")
+    _need(k_cache.dim() == 4, "caches must be [batch, kv_heads, g + w, d]")
+    Hkv = k_cache.shape[1]
+    _need(k_cache.shape == v_cache.shape == (B, Hkv, g + w, d), f"caches must be [batch, kv_heads, g + w, d]")
     _need(q.dtype == k_cache.dtype == v_cache.dtype, "one dtype for q and the caches")
     _need(pos.dtype == torch.int64 and pos.shape == (B,), "pos must be int64 [batch]")
     if scale is None:
@@ -166,16 +185,17 @@ def decode(q, k_cache, v_cache, pos, w: int, g: int = 0, scale: float | None = N
     _dev_tensor(o, "out")
     _need(o.shape == q.shape and o.dtype == q.dtype, "out must match q")
     lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if return_lse else None
-    need = decode_workspace_bytes(B, H, d, w, g)
+    need = decode_workspace_bytes(B, H, d, w, g, kv_heads=Hkv)
     if need > 0 and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    rc = lib().swa_decode_fwd(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), pos.data_ptr(), o.data_ptr(),
-                              lse.data_ptr() if lse is not None else None, B, H, d, int(w), int(g),
-                              float(scale), float(sink_bias), _dtype_code(q), ws_ptr, ws_bytes, _stream(q))
+    rc = lib().swa_decode_fwd_gqa(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), pos.data_ptr(),
+                                  o.data_ptr(), lse.data_ptr() if lse is not None else None, B, H, Hkv, d,
+                                  int(w), int(g), float(scale), float(sink_bias), _dtype_code(q), ws_ptr, ws_bytes,
+                                  _stream(q))
     if rc != 0:
-        raise SwaError(rc, "swa_decode_fwd")
+        raise SwaError(rc, "swa_decode_fwd_gqa")
     return (o, lse) if return_lse else o
 
 

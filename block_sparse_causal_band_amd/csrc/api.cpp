@@ -10,14 +10,15 @@
 #include "schedule.h"
 
 namespace swa {
-hipError_t launch_prefill(const void *q, const void *k, const void *v, void *o, float *lse, int units, int n,
-                          int d, int w, int g, float scale, float sink_bias, bool bf16, hipStream_t stream);
+hipError_t launch_prefill(const void *q, const void *k, const void *v, void *o, float *lse, int batch, int heads,
+                          int kv_heads, int n, int d, int w, int g, float scale, float sink_bias, bool bf16,
+                          hipStream_t stream);
 hipError_t launch_decode(const void *q, const void *kc, const void *vc, const int64_t *pos, void *o, float *lse,
-                         int units, int heads, int d, int w, int g, float scale, float sink_bias, bool bf16,
-                         void *ws, hipStream_t stream);
+                         int batch, int heads, int kv_heads, int d, int w, int g, float scale, float sink_bias,
+                         bool bf16, void *ws, hipStream_t stream);
 hipError_t launch_kv_append(void *kc, void *vc, const void *kn, const void *vn, const int64_t *pos, int batch,
                             int heads, int tn, int d, int w, int g, bool bf16, hipStream_t stream);
-size_t decode_workspace_bytes(int units, int d, int rows);
+size_t decode_workspace_bytes(int batch, int heads, int kv_heads, int d, int rows);
 int prefill_rows_per_workgroup(bool bf16);
 // keys per prefill tile (prefill.hip)
 constexpr int kPrefillBK = 64;
@@ -53,10 +54,12 @@ const char *swa_strerror(int status) {
     }
 }
 
-int swa_prefill_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int batch, int heads, int n,
-                    int d, int w, int g, float scale, float sink_bias, swa_dtype_t dtype, hipStream_t stream) {
+int swa_prefill_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse, int batch, int heads,
+                        int kv_heads, int n, int d, int w, int g, float scale, float sink_bias, swa_dtype_t dtype,
+                        hipStream_t stream) {
     if (!q || !k || !v || !o) return SWA_EINVAL;
     if (batch < 1 || heads < 1 || n < 1 || w < 1 || g < 0) return SWA_EINVAL;
+    if (kv_heads < 1 || kv_heads > heads || heads % kv_heads != 0) return SWA_EINVAL;
     if (!std::isfinite(scale) || !(scale > 0.f) || !std::isfinite(sink_bias)) return SWA_EINVAL;
     int st = check_dtype_d(dtype, d);
     if (st != SWA_OK) return st;
@@ -67,8 +70,13 @@ int swa_prefill_fwd(const void *q, const void *k, const void *v, void *o, float 
     if (units * nqb > INT_MAX) return SWA_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned4(lse)))
         return SWA_EALIGN;
-    return status_of(swa::launch_prefill(q, k, v, o, lse, (int)units, n, d, w, g, scale, sink_bias,
+    return status_of(swa::launch_prefill(q, k, v, o, lse, batch, heads, kv_heads, n, d, w, g, scale, sink_bias,
                                          dtype == SWA_BF16, stream));
+}
+
+int swa_prefill_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int batch, int heads, int n,
+                    int d, int w, int g, float scale, float sink_bias, swa_dtype_t dtype, hipStream_t stream) {
+    return swa_prefill_fwd_gqa(q, k, v, o, lse, batch, heads, heads, n, d, w, g, scale, sink_bias, dtype, stream);
 }
 
 int swa_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v_new, const int64_t *pos,
@@ -88,16 +96,24 @@ int swa_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v
                                            dtype == SWA_BF16, stream));
 }
 
-size_t swa_decode_workspace_bytes(int batch, int heads, int d, int w, int g) {
+size_t swa_decode_workspace_bytes_gqa(int batch, int heads, int kv_heads, int d, int w, int g) {
     if (batch < 1 || heads < 1 || w < 1 || g < 0 || (d != 64 && d != 128)) return 0;
-    return swa::decode_workspace_bytes(batch * heads, d, g + w);
+    if (kv_heads < 1 || kv_heads > heads || heads % kv_heads != 0) return 0;
+    if ((long long)g + w > INT_MAX / 2 || (long long)batch * heads > INT_MAX / 64) return 0;
+    return swa::decode_workspace_bytes(batch, heads, kv_heads, d, g + w);
 }
 
-int swa_decode_fwd(const void *q, const void *k_cache, const void *v_cache, const int64_t *pos, void *o, float *lse,
-                   int batch, int heads, int d, int w, int g, float scale, float sink_bias, swa_dtype_t dtype,
-                   void *workspace, size_t workspace_bytes, hipStream_t stream) {
+size_t swa_decode_workspace_bytes(int batch, int heads, int d, int w, int g) {
+    return swa_decode_workspace_bytes_gqa(batch, heads, heads, d, w, g);
+}
+
+int swa_decode_fwd_gqa(const void *q, const void *k_cache, const void *v_cache, const int64_t *pos, void *o,
+                       float *lse, int batch, int heads, int kv_heads, int d, int w, int g, float scale,
+                       float sink_bias, swa_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
     if (!q || !k_cache || !v_cache || !pos || !o) return SWA_EINVAL;
     if (batch < 1 || heads < 1 || w < 1 || g < 0) return SWA_EINVAL;
+    if (kv_heads < 1 || kv_heads > heads || heads % kv_heads != 0) return SWA_EINVAL;
     if ((long long)g + w > INT_MAX / 2) return SWA_EINVAL;
     if ((long long)batch * heads > INT_MAX / 64) return SWA_EINVAL;
     if (!std::isfinite(scale) || !(scale > 0.f) || !std::isfinite(sink_bias)) return SWA_EINVAL;
@@ -106,13 +122,20 @@ int swa_decode_fwd(const void *q, const void *k_cache, const void *v_cache, cons
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
         (reinterpret_cast<uintptr_t>(pos) & 7u) || (lse && !aligned4(lse)))
         return SWA_EALIGN;
-    const size_t need = swa::decode_workspace_bytes(batch * heads, d, g + w);
+    const size_t need = swa::decode_workspace_bytes(batch, heads, kv_heads, d, g + w);
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return SWA_EWORKSPACE;
         if (!aligned16(workspace)) return SWA_EALIGN;
     }
-    return status_of(swa::launch_decode(q, k_cache, v_cache, pos, o, lse, batch * heads, heads, d, w, g, scale,
+    return status_of(swa::launch_decode(q, k_cache, v_cache, pos, o, lse, batch, heads, kv_heads, d, w, g, scale,
                                         sink_bias, dtype == SWA_BF16, workspace, stream));
+}
+
+int swa_decode_fwd(const void *q, const void *k_cache, const void *v_cache, const int64_t *pos, void *o, float *lse,
+                   int batch, int heads, int d, int w, int g, float scale, float sink_bias, swa_dtype_t dtype,
+                   void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return swa_decode_fwd_gqa(q, k_cache, v_cache, pos, o, lse, batch, heads, heads, d, w, g, scale, sink_bias, dtype,
+                              workspace, workspace_bytes, stream);
 }
 
 long swa_band_tiles(int n, int w, int g, int bq, int bk, int *out, long cap) {

@@ -70,12 +70,15 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
-// Partial state of one workgroup: m (raw q.k units incl. bias), l, o[D] (unnormalised).
-template <bool BF16, int D>
+// Partial state of one workgroup: m (raw q.k units incl. bias), l, o[D]
+// (unnormalised), for each of its GQ query heads.  The GQ query heads share
+// one key/value head (grouped-query attention), so each cache row is read
+// once for all of them.
+template <bool BF16, int D, int GQ>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const void *__restrict__ qp, const void *__restrict__ kcp, const void *__restrict__ vcp,
-    const int64_t *__restrict__ pos, void *__restrict__ op, float *__restrict__ lsep, int heads, int w,
-    int g, float c2, float scale, float bias_raw, int splits, int rows_per_split, float *__restrict__ ws) {
+    const int64_t *__restrict__ pos, void *__restrict__ op, float *__restrict__ lsep, int heads, int kv_heads,
+    int w, int g, float c2, float scale, float bias_raw, int splits, int rows_per_split, float *__restrict__ ws) {
     using C = DecodeCfg<BF16, D>;
     using T = typename C::T;
     constexpr int EPC = C::kEPC, LPR = C::kLPR, RPI = C::kRPI;
@@ -86,27 +89,39 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const int grp_in_wave = lane / LPR, sub = lane % LPR;
     const int group = wave * RPI + grp_in_wave;
     const int split = blockIdx.x % splits;
-    const int unit = blockIdx.x / splits;  // batch * heads + head
-    const int b = unit / heads;
+    const int job = blockIdx.x / splits;       // (batch, kv head, chunk of GQ query heads)
+    const int chunks = heads / kv_heads / GQ;  // query-head chunks per kv head
+    const int chunk = job % chunks;
+    const int kvu = job / chunks;              // batch * kv_heads + kv head
+    const int b = kvu / kv_heads;
+    const int h0 = (kvu % kv_heads) * (heads / kv_heads) + chunk * GQ;  // first query head
+    const int unit0 = b * heads + h0;          // batch * heads + query head of head 0
     const int R = g + w;
     const int64_t p = pos[b];
 
-    const T *q = reinterpret_cast<const T *>(qp) + (size_t)unit * D;
-    const T *kc = reinterpret_cast<const T *>(kcp) + (size_t)unit * R * D;
-    const T *vc = reinterpret_cast<const T *>(vcp) + (size_t)unit * R * D;
+    const T *kc = reinterpret_cast<const T *>(kcp) + (size_t)kvu * R * D;
+    const T *vc = reinterpret_cast<const T *>(vcp) + (size_t)kvu * R * D;
 
-    float qf[EPC];
-    unpack<BF16>(*reinterpret_cast<const uint4 *>(q + sub * EPC), qf);
+    float qf[GQ][EPC];
+#pragma unroll
+    for (int j = 0; j < GQ; ++j) {
+        const T *q = reinterpret_cast<const T *>(qp) + (size_t)(unit0 + j) * D;
+        unpack<BF16>(*reinterpret_cast<const uint4 *>(q + sub * EPC), qf[j]);
+    }
 
     // ring geometry for this query position
     const bool ring_full = (p >= (int64_t)w - 1);
     const int pm = (p >= 0) ? (int)(p % w) : 0;  // slot of the query itself
     const int64_t win_lo = p - w + 1;           // first window position
 
-    float m = kNegInf, l = 0.f;
-    float o[EPC];
+    float m[GQ], l[GQ], o[GQ][EPC];
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) o[e] = 0.f;
+    for (int j = 0; j < GQ; ++j) {
+        m[j] = kNegInf;
+        l[j] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) o[j][e] = 0.f;
+    }
 
     const int r_begin = split * rows_per_split;
     const int r_end = min(R, r_begin + rows_per_split);
@@ -125,15 +140,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                 vx[u] = make_uint4(0, 0, 0, 0);
             }
         }
-        float s[kDecUnroll];
+        float s[GQ][kDecUnroll];
 #pragma unroll
         for (int u = 0; u < kDecUnroll; ++u) {
-            float kf[EPC];
-            unpack<BF16>(kx[u], kf);
-            float acc = 0.f;
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) acc = fmaf(qf[e], kf[e], acc);
-            acc = group_sum<LPR>(acc);
             // which position does row r hold, and is it read?
             int r = rows[u];
             bool valid;
@@ -156,72 +165,90 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                     valid = (sl <= p);
                 }
             }
-            if (t < g) acc += bias_raw;
-            s[u] = valid ? acc : kNegInf;
+            const float bias = (t < g) ? bias_raw : 0.f;
+            float kf[EPC];
+            unpack<BF16>(kx[u], kf);
+#pragma unroll
+            for (int j = 0; j < GQ; ++j) {
+                float acc = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) acc = fmaf(qf[j][e], kf[e], acc);
+                acc = group_sum<LPR>(acc) + bias;
+                s[j][u] = valid ? acc : kNegInf;
+            }
         }
-        float mx = s[0];
+        float vf[kDecUnroll][EPC];
 #pragma unroll
-        for (int u = 1; u < kDecUnroll; ++u) mx = fmaxf(mx, s[u]);
-        const float m_new = fmaxf(m, mx);
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = fast_exp2((m - m_use) * c2);
-        const float neg = -m_use * c2;
-        l *= alpha;
+        for (int u = 0; u < kDecUnroll; ++u) unpack<BF16>(vx[u], vf[u]);
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) o[e] *= alpha;
+        for (int j = 0; j < GQ; ++j) {
+            float mx = s[j][0];
 #pragma unroll
-        for (int u = 0; u < kDecUnroll; ++u) {
-            float pu = fast_exp2(fmaf(s[u], c2, neg));
-            l += pu;
-            float vf[EPC];
-            unpack<BF16>(vx[u], vf);
+            for (int u = 1; u < kDecUnroll; ++u) mx = fmaxf(mx, s[j][u]);
+            const float m_new = fmaxf(m[j], mx);
+            const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+            const float alpha = fast_exp2((m[j] - m_use) * c2);
+            const float neg = -m_use * c2;
+            l[j] *= alpha;
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) o[e] = fmaf(pu, vf[e], o[e]);
+            for (int e = 0; e < EPC; ++e) o[j][e] *= alpha;
+#pragma unroll
+            for (int u = 0; u < kDecUnroll; ++u) {
+                const float pu = fast_exp2(fmaf(s[j][u], c2, neg));
+                l[j] += pu;
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) o[j][e] = fmaf(pu, vf[u][e], o[j][e]);
+            }
+            m[j] = m_new;
         }
-        m = m_new;
     }
 
-    // ---- merge the row groups of this workgroup ----
-    if (sub == 0) {
-        sh_m[group] = m;
-        sh_l[group] = l;
-    }
+    // ---- merge the row groups of this workgroup, one query head at a time ----
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) sh_o[group][sub * EPC + e] = o[e];
-    __syncthreads();
-    float M = kNegInf;
+    for (int j = 0; j < GQ; ++j) {
+        const int unit = unit0 + j;
+        if (j > 0) __syncthreads();  // the previous head's merge has read the LDS
+        if (sub == 0) {
+            sh_m[group] = m[j];
+            sh_l[group] = l[j];
+        }
 #pragma unroll
-    for (int gi = 0; gi < C::kGroups; ++gi) M = fmaxf(M, sh_m[gi]);
-    const float M_use = (M == kNegInf) ? 0.f : M;
-    float L = 0.f;
+        for (int e = 0; e < EPC; ++e) sh_o[group][sub * EPC + e] = o[j][e];
+        __syncthreads();
+        float M = kNegInf;
 #pragma unroll
-    for (int gi = 0; gi < C::kGroups; ++gi) L += sh_l[gi] * fast_exp2((sh_m[gi] - M_use) * c2);
+        for (int gi = 0; gi < C::kGroups; ++gi) M = fmaxf(M, sh_m[gi]);
+        const float M_use = (M == kNegInf) ? 0.f : M;
+        float L = 0.f;
+#pragma unroll
+        for (int gi = 0; gi < C::kGroups; ++gi) L += sh_l[gi] * fast_exp2((sh_m[gi] - M_use) * c2);
 
-    if (splits == 1) {
-        const float inv = (L > 0.f) ? 1.f / L : __builtin_nanf("");
-        T *out = reinterpret_cast<T *>(op) + (size_t)unit * D;
-        for (int c = tid; c < D; c += kDecThreads) {
-            float acc = 0.f;
+        if (splits == 1) {
+            const float inv = (L > 0.f) ? 1.f / L : __builtin_nanf("");
+            T *out = reinterpret_cast<T *>(op) + (size_t)unit * D;
+            for (int c = tid; c < D; c += kDecThreads) {
+                float acc = 0.f;
 #pragma unroll
-            for (int gi = 0; gi < C::kGroups; ++gi) acc += sh_o[gi][c] * fast_exp2((sh_m[gi] - M_use) * c2);
-            float x = acc * inv;
-            if constexpr (BF16)
-                out[c] = (uint16_t)f32_to_bf16_bits(x);
-            else
-                out[c] = x;
-        }
-        if (lsep != nullptr && tid == 0) lsep[unit] = (L > 0.f) ? M * scale + logf(L) : __builtin_nanf("");
-    } else {
-        float *rec = ws + ((size_t)unit * splits + split) * (2 + D);
-        for (int c = tid; c < D; c += kDecThreads) {
-            float acc = 0.f;
+                for (int gi = 0; gi < C::kGroups; ++gi) acc += sh_o[gi][c] * fast_exp2((sh_m[gi] - M_use) * c2);
+                float x = acc * inv;
+                if constexpr (BF16)
+                    out[c] = (uint16_t)f32_to_bf16_bits(x);
+                else
+                    out[c] = x;
+            }
+            if (lsep != nullptr && tid == 0) lsep[unit] = (L > 0.f) ? M * scale + logf(L) : __builtin_nanf("");
+        } else {
+            float *rec = ws + ((size_t)unit * splits + split) * (2 + D);
+            for (int c = tid; c < D; c += kDecThreads) {
+                float acc = 0.f;
 #pragma unroll
-            for (int gi = 0; gi < C::kGroups; ++gi) acc += sh_o[gi][c] * fast_exp2((sh_m[gi] - M_use) * c2);
-            rec[2 + c] = acc;
-        }
-        if (tid == 0) {
-            rec[0] = M;
-            rec[1] = L;
+                for (int gi = 0; gi < C::kGroups; ++gi) acc += sh_o[gi][c] * fast_exp2((sh_m[gi] - M_use) * c2);
+                rec[2 + c] = acc;
+            }
+            if (tid == 0) {
+                rec[0] = M;
+                rec[1] = L;
+            }
         }
     }
 }
@@ -253,10 +280,18 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float *__restrict
     if (lsep != nullptr && c == 0) lsep[unit] = (L > 0.f) ? M * scale + logf(L) : __builtin_nanf("");
 }
 
+// Query heads per decode workgroup: the largest power of two <= 8 that
+// divides the group size (query heads per key/value head).
+int decode_heads_per_wg(int group) {
+    int gq = 1;
+    while (gq < 8 && group % (2 * gq) == 0) gq *= 2;
+    return gq;
+}
+
 // Split count: enough workgroups to cover the chip, at least 256 cache rows each.
-int decode_splits(int units, int rows) {
-    if (units >= 1024) return 1;
-    int s = (2048 + units - 1) / units;
+int decode_splits(int jobs, int rows) {
+    if (jobs >= 1024) return 1;
+    int s = (2048 + jobs - 1) / jobs;
     int max_s = rows / 256;
     if (max_s < 1) max_s = 1;
     if (s > max_s) s = max_s;
@@ -264,39 +299,57 @@ int decode_splits(int units, int rows) {
     return s < 1 ? 1 : s;
 }
 
-size_t decode_workspace_bytes(int units, int d, int rows) {
-    int s = decode_splits(units, rows);
-    if (s == 1) return 0;
-    return (size_t)units * s * (2 + d) * sizeof(float);
+// jobs = batch * heads / (query heads per workgroup): workgroups before splitting
+static int decode_jobs(int batch, int heads, int kv_heads) {
+    return batch * (heads / decode_heads_per_wg(heads / kv_heads));
 }
 
-template <bool BF16, int D>
+size_t decode_workspace_bytes(int batch, int heads, int kv_heads, int d, int rows) {
+    int s = decode_splits(decode_jobs(batch, heads, kv_heads), rows);
+    if (s == 1) return 0;
+    return (size_t)batch * heads * s * (2 + d) * sizeof(float);
+}
+
+template <bool BF16, int D, int GQ>
 static hipError_t launch_decode_t(const void *q, const void *kc, const void *vc, const int64_t *pos, void *o,
-                                  float *lse, int units, int heads, int w, int g, float scale, float sink_bias,
-                                  void *ws, hipStream_t stream) {
+                                  float *lse, int batch, int heads, int kv_heads, int w, int g, float scale,
+                                  float sink_bias, void *ws, hipStream_t stream) {
     const int R = g + w;
-    const int splits = decode_splits(units, R);
+    const int jobs = decode_jobs(batch, heads, kv_heads);
+    const int splits = decode_splits(jobs, R);
     const int rps = (R + splits - 1) / splits;
     const float c2 = (float)((double)scale * kLog2e);
     const float bias_raw = (float)((double)sink_bias / (double)scale);
-    hipLaunchKernelGGL((decode_kernel<BF16, D>), dim3(units * splits), dim3(kDecThreads), 0, stream, q, kc, vc, pos,
-                       o, lse, heads, w, g, c2, scale, bias_raw, splits, rps, (float *)ws);
+    hipLaunchKernelGGL((decode_kernel<BF16, D, GQ>), dim3(jobs * splits), dim3(kDecThreads), 0, stream, q, kc, vc,
+                       pos, o, lse, heads, kv_heads, w, g, c2, scale, bias_raw, splits, rps, (float *)ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
-    hipLaunchKernelGGL((decode_merge_kernel<BF16, D>), dim3(units), dim3(D), 0, stream, (const float *)ws, o, lse,
-                       splits, c2, scale);
+    hipLaunchKernelGGL((decode_merge_kernel<BF16, D>), dim3(batch * heads), dim3(D), 0, stream, (const float *)ws,
+                       o, lse, splits, c2, scale);
     return hipGetLastError();
 }
 
-hipError_t launch_decode(const void *q, const void *kc, const void *vc, const int64_t *pos, void *o, float *lse,
-                         int units, int heads, int d, int w, int g, float scale, float sink_bias, bool bf16,
-                         void *ws, hipStream_t stream) {
-    if (bf16) {
-        if (d == 128) return launch_decode_t<true, 128>(q, kc, vc, pos, o, lse, units, heads, w, g, scale, sink_bias, ws, stream);
-        return launch_decode_t<true, 64>(q, kc, vc, pos, o, lse, units, heads, w, g, scale, sink_bias, ws, stream);
+template <bool BF16, int D>
+static hipError_t launch_decode_d(const void *q, const void *kc, const void *vc, const int64_t *pos, void *o,
+                                  float *lse, int batch, int heads, int kv_heads, int w, int g, float scale,
+                                  float sink_bias, void *ws, hipStream_t stream) {
+    switch (decode_heads_per_wg(heads / kv_heads)) {
+        case 8: return launch_decode_t<BF16, D, 8>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale, sink_bias, ws, stream);
+        case 4: return launch_decode_t<BF16, D, 4>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale, sink_bias, ws, stream);
+        case 2: return launch_decode_t<BF16, D, 2>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale, sink_bias, ws, stream);
+        default: return launch_decode_t<BF16, D, 1>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale, sink_bias, ws, stream);
     }
-    if (d == 128) return launch_decode_t<false, 128>(q, kc, vc, pos, o, lse, units, heads, w, g, scale, sink_bias, ws, stream);
-    return launch_decode_t<false, 64>(q, kc, vc, pos, o, lse, units, heads, w, g, scale, sink_bias, ws, stream);
+}
+
+hipError_t launch_decode(const void *q, const void *kc, const void *vc, const int64_t *pos, void *o, float *lse,
+                         int batch, int heads, int kv_heads, int d, int w, int g, float scale, float sink_bias,
+                         bool bf16, void *ws, hipStream_t stream) {
+    if (bf16) {
+        if (d == 128) return launch_decode_d<true, 128>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale, sink_bias, ws, stream);
+        return launch_decode_d<true, 64>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale, sink_bias, ws, stream);
+    }
+    if (d == 128) return launch_decode_d<false, 128>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale, sink_bias, ws, stream);
+    return launch_decode_d<false, 64>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale, sink_bias, ws, stream);
 }
 
 // ---------------------------------------------------------------------------

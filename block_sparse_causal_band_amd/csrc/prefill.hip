@@ -67,6 +67,14 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t *p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((SWA_LDS s16x4 *)p);
 }
 
+// Element offset of the key/value rows that query unit (batch * heads + head)
+// reads: grouped-query attention maps heads / kv_heads consecutive query heads
+// onto one key/value head (kv_heads == heads is plain multi-head attention).
+__device__ __forceinline__ size_t kv_offset(int unit, int heads, int kv_heads, int n, int d) {
+    const int b = unit / heads, h = unit - b * heads;
+    return ((size_t)b * kv_heads + h / (heads / kv_heads)) * n * d;
+}
+
 // ---------------------------------------------------------------------------
 // Pieces shared by both paths.  s[sb][r] holds q_qi . k_j for the key
 // j = k0 + 32 sb + 8 (r/4) + 4 lh + r%4 (the 32x32 MFMA result layout).
@@ -170,7 +178,7 @@ template <int D, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp, const uint16_t *__restrict__ vp,
     uint16_t *__restrict__ op, float *__restrict__ lsep, int n, int nqb, int w, int g, float c2, float scale,
-    float bias_raw, int total_wg) {
+    float bias_raw, int total_wg, int heads, int kv_heads) {
     using L = Bf16Tile<D, WAVES>;
     constexpr int BQ = 32 * WAVES;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * L::kStageBytes];
@@ -183,10 +191,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
 
     int unit, qb;
     workgroup_order(blockIdx.x, total_wg, nqb, &unit, &qb);
-    const size_t base = (size_t)unit * n * D;
+    const size_t base = (size_t)unit * n * D;  // q and o of (batch, head)
     const uint16_t *Q = qp + base;
-    const uint16_t *K = kp + base;
-    const uint16_t *V = vp + base;
+    const uint16_t *K = kp + kv_offset(unit, heads, kv_heads, n, D);
+    const uint16_t *V = vp + kv_offset(unit, heads, kv_heads, n, D);
 
     const int q0 = qb * BQ;
     const int q1 = min(q0 + BQ, n) - 1;
@@ -456,7 +464,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
     const float *__restrict__ qp, const float *__restrict__ kp, const float *__restrict__ vp,
     float *__restrict__ op, float *__restrict__ lsep, int n, int nqb, int w, int g, float c2, float scale,
-    float bias_raw, int total_wg) {
+    float bias_raw, int total_wg, int heads, int kv_heads) {
     using C = F32Cfg<D>;
     __shared__ __attribute__((aligned(16))) float smem[2 * C::kStage];
 
@@ -468,10 +476,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
 
     int unit, qb;
     workgroup_order(blockIdx.x, total_wg, nqb, &unit, &qb);
-    const size_t base = (size_t)unit * n * D;
+    const size_t base = (size_t)unit * n * D;  // q and o of (batch, head)
     const float *Q = qp + base;
-    const float *K = kp + base;
-    const float *V = vp + base;
+    const float *K = kp + kv_offset(unit, heads, kv_heads, n, D);
+    const float *V = vp + kv_offset(unit, heads, kv_heads, n, D);
 
     const int q0 = qb * kBQ;
     const int q1 = min(q0 + kBQ, n) - 1;
@@ -570,8 +578,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
 int prefill_rows_per_workgroup(bool bf16) { return bf16 ? 32 * kWaves16 : kBQ; }
 
 // Host launcher (validated arguments only).
-hipError_t launch_prefill(const void *q, const void *k, const void *v, void *o, float *lse, int units, int n, int d,
-                          int w, int g, float scale, float sink_bias, bool bf16, hipStream_t stream) {
+hipError_t launch_prefill(const void *q, const void *k, const void *v, void *o, float *lse, int batch, int heads,
+                          int kv_heads, int n, int d, int w, int g, float scale, float sink_bias, bool bf16,
+                          hipStream_t stream) {
+    const int units = batch * heads;
     const float c2 = (float)((double)scale * kLog2e);
     const float bias_raw = (float)((double)sink_bias / (double)scale);
     if (bf16) {
@@ -583,10 +593,10 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, void *o, 
         uint16_t *oo = (uint16_t *)o;
         if (d == 128)
             hipLaunchKernelGGL((prefill_bf16_kernel<128, kWaves16>), grid, block, 0, stream, qq, kk, vv, oo, lse, n,
-                               nqb, w, g, c2, scale, bias_raw, total);
+                               nqb, w, g, c2, scale, bias_raw, total, heads, kv_heads);
         else
             hipLaunchKernelGGL((prefill_bf16_kernel<64, kWaves16>), grid, block, 0, stream, qq, kk, vv, oo, lse, n,
-                               nqb, w, g, c2, scale, bias_raw, total);
+                               nqb, w, g, c2, scale, bias_raw, total, heads, kv_heads);
     } else {
         const int nqb = (n + kBQ - 1) / kBQ;
         const int total = units * nqb;
@@ -595,10 +605,10 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, void *o, 
         float *oo = (float *)o;
         if (d == 128)
             hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, block, 0, stream, qq, kk, vv, oo, lse, n, nqb, w, g, c2,
-                               scale, bias_raw, total);
+                               scale, bias_raw, total, heads, kv_heads);
         else
             hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, block, 0, stream, qq, kk, vv, oo, lse, n, nqb, w, g, c2,
-                               scale, bias_raw, total);
+                               scale, bias_raw, total, heads, kv_heads);
     }
     return hipGetLastError();
 }

@@ -30,23 +30,26 @@ def normal(shape, seed: int, dtype=torch.float32, device="cpu") -> torch.Tensor:
     return torch.randn(*shape, generator=g, dtype=torch.float32, device=device).to(dtype)
 
 
-def qkv(batch: int, heads: int, n: int, d: int, dtype, seed: int, device="cpu"):
-    """Q, K, V of shape [batch, heads, n, d], iid N(0, 1), rounded to dtype."""
+def qkv(batch: int, heads: int, n: int, d: int, dtype, seed: int, device="cpu", kv_heads: int | None = None):
+    """Q [batch, heads, n, d] and K, V [batch, kv_heads (default heads), n, d],
+    iid N(0, 1), rounded to dtype."""
     g = _gen(seed, device)
-    shape = (batch, heads, n, d)
     out = []
-    for _ in range(3):
-        out.append(torch.randn(*shape, generator=g, dtype=torch.float32, device=device).to(dtype))
+    for i in range(3):
+        hh = heads if (i == 0 or kv_heads is None) else kv_heads
+        out.append(torch.randn(batch, hh, n, d, generator=g, dtype=torch.float32, device=device).to(dtype))
     return tuple(out)
 
 
 def decode_problem(batch: int, heads: int, d: int, rows: int, lo: int, hi: int, dtype,
-                   seed: int, device="cpu"):
-    """(q [B,H,d], k_cache [B,H,rows,d], v_cache [B,H,rows,d], pos [B] int64 in [lo, hi])."""
+                   seed: int, device="cpu", kv_heads: int | None = None):
+    """(q [B,H,d], k_cache [B,Hkv,rows,d], v_cache [B,Hkv,rows,d], pos [B] int64
+    in [lo, hi]); Hkv = kv_heads, default H."""
     g = _gen(seed, device)
+    hk = heads if kv_heads is None else kv_heads
     q = torch.randn(batch, heads, d, generator=g, dtype=torch.float32, device=device).to(dtype)
-    kc = torch.randn(batch, heads, rows, d, generator=g, dtype=torch.float32, device=device).to(dtype)
-    vc = torch.randn(batch, heads, rows, d, generator=g, dtype=torch.float32, device=device).to(dtype)
+    kc = torch.randn(batch, hk, rows, d, generator=g, dtype=torch.float32, device=device).to(dtype)
+    vc = torch.randn(batch, hk, rows, d, generator=g, dtype=torch.float32, device=device).to(dtype)
     gp = _gen(seed + 1, "cpu")
     pos = torch.randint(lo, hi + 1, (batch,), generator=gp, dtype=torch.int64).to(device)
     return q, kc, vc, pos

@@ -120,6 +120,32 @@ int swa_decode_fwd(const void *q, const void *k_cache, const void *v_cache, cons
  * does not split the cache rows of one (batch, head) across workgroups). */
 size_t swa_decode_workspace_bytes(int batch, int heads, int d, int w, int g);
 
+/*
+ * Grouped-query attention ("Sliding Window and Sparse Attention, from
+ * Longformer to CSA2", s10 glossary, GQA: several query heads share one
+ * key/value head, which shrinks the KV cache by the group size): kv_heads
+ * key/value heads serve heads query heads, heads % kv_heads == 0, and query
+ * head h reads key/value head h / (heads / kv_heads).  kv_heads == heads is the plain calls above (which
+ * forward here); kv_heads == 1 is multi-query attention.  Shapes:
+ *   prefill: q, o [batch][heads][n][d]; k, v [batch][kv_heads][n][d];
+ *            lse [batch][heads][n]
+ *   decode:  q, o [batch][heads][d]; caches [batch][kv_heads][g + w][d]
+ *            (written by swa_kv_append with its `heads` = kv_heads);
+ *            lse [batch][heads]
+ * Everything else (validation, layout, ownership, errors) is as for the
+ * plain calls; an invalid kv_heads is SWA_EINVAL.  Decode reads each cache
+ * row once for up to 8 query heads of its group (one workgroup serves them).
+ */
+int swa_prefill_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse,
+                        int batch, int heads, int kv_heads, int n, int d, int w, int g,
+                        float scale, float sink_bias, swa_dtype_t dtype, hipStream_t stream);
+int swa_decode_fwd_gqa(const void *q, const void *k_cache, const void *v_cache, const int64_t *pos,
+                       void *o, float *lse, int batch, int heads, int kv_heads, int d, int w, int g,
+                       float scale, float sink_bias, swa_dtype_t dtype,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+/* Workspace bytes of swa_decode_fwd_gqa (0 also for an invalid shape). */
+size_t swa_decode_workspace_bytes_gqa(int batch, int heads, int kv_heads, int d, int w, int g);
+
 /* Static description of a status code. */
 const char *swa_strerror(int status);
 

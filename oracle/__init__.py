@@ -20,6 +20,10 @@ Sources (page title, then the section / figure used):
   * "Local and Sparse Attention: Reading Fewer Token Positions": Figures 1, 2
     and 4 and the text between them (window of 3 counts the current token;
     -inf masking, not zeroing; anchor union read once; eviction).
+  * "Sliding Window and Sparse Attention, from Longformer to CSA2", s10
+    glossary, GQA: several query heads share one key/value head.  The page
+    does not say which ones; the reading taken here is consecutive groups,
+    query head h of H reading key/value head h // (H / Hkv) (``kv_head_of``).
 """
 from __future__ import annotations
 
@@ -105,8 +109,13 @@ class Oracle:
 
         q, k, v: [..., n, d] (any leading batch/head dims).  ``rows``: the query
         rows to evaluate (default: all).  Returns (o [..., nrows, d], lse [..., nrows]).
+        Grouped-query attention: q [..., H, n, d] with k, v [..., Hkv, n, d],
+        Hkv dividing H; each query head is paired with its key/value head
+        (``kv_head_of``) before the rows are evaluated.
         """
         q, k, v = _f64(q), _f64(k), _f64(v)
+        if k.shape == v.shape and k.shape != q.shape and q.ndim >= 3:
+            k, v = expand_kv_heads(q.shape[-3], k), expand_kv_heads(q.shape[-3], v)
         if q.shape != k.shape or q.shape != v.shape or q.ndim < 2:
             raise ValueError("q, k, v must share one shape [..., n, d]")
         lead = q.shape[:-2]
@@ -153,6 +162,22 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"swa_oracle_decode failed ({rc})")
         return o, lse
+
+
+def kv_head_of(h: int, heads: int, kv_heads: int) -> int:
+    """Key/value head read by query head h when kv_heads of them serve heads
+    query heads (grouped-query attention, consecutive groups)."""
+    if kv_heads < 1 or heads % kv_heads != 0 or not 0 <= h < heads:
+        raise ValueError("kv_heads must divide heads and 0 <= h < heads")
+    return h // (heads // kv_heads)
+
+
+def expand_kv_heads(heads: int, x: np.ndarray) -> np.ndarray:
+    """x [..., Hkv, n, d] -> [..., heads, n, d] with query head h holding
+    x[..., kv_head_of(h), :, :]."""
+    kv_heads = x.shape[-3]
+    idx = [kv_head_of(h, heads, kv_heads) for h in range(heads)]
+    return np.ascontiguousarray(np.take(x, idx, axis=-3))
 
 
 _DEFAULT: Oracle | None = None

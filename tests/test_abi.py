@@ -104,3 +104,47 @@ def test_decode_workspace_sizes():
     need = swa.decode_workspace_bytes(1, 1, 128, 4096, 4)
     assert need > 0 and need % 16 == 0
     assert swa.decode_workspace_bytes(1, 1, 96, 4096, 4) == 0           # unsupported d: nothing to size
+
+
+def _prefill_gqa(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, batch=1, heads=8, kv_heads=2, n=16, d=128, w=4, g=0,
+             scale=0.125, bias=0.0, dtype=1)
+    a.update(kw)
+    return swa.lib().swa_prefill_fwd_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["batch"], a["heads"],
+                                         a["kv_heads"], a["n"], a["d"], a["w"], a["g"], a["scale"], a["bias"],
+                                         a["dtype"], None)
+
+
+def _decode_gqa(**kw):
+    a = dict(q=P, kc=P, vc=P, pos=P, o=P, lse=None, batch=64, heads=32, kv_heads=8, d=128, w=4096, g=4,
+             scale=0.125, bias=0.0, dtype=1, ws=None, wsb=0)
+    a.update(kw)
+    return swa.lib().swa_decode_fwd_gqa(a["q"], a["kc"], a["vc"], a["pos"], a["o"], a["lse"], a["batch"],
+                                        a["heads"], a["kv_heads"], a["d"], a["w"], a["g"], a["scale"], a["bias"],
+                                        a["dtype"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(kv_heads=0), EINVAL), (dict(kv_heads=3), EINVAL), (dict(kv_heads=16), EINVAL),
+    (dict(kv_heads=-2), EINVAL), (dict(k=None), EINVAL), (dict(d=80), EUNSUP), (dict(v=P + 8), EALIGN),
+])
+def test_prefill_gqa_rejects(kw, want):
+    assert _prefill_gqa(**kw) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(kv_heads=0), EINVAL), (dict(kv_heads=5), EINVAL), (dict(kv_heads=64), EINVAL),
+    (dict(kc=None), EINVAL), (dict(dtype=2), EUNSUP),
+    (dict(batch=1, heads=8, kv_heads=1), EWS),  # one workgroup's worth of heads: split, needs a workspace
+])
+def test_decode_gqa_rejects(kw, want):
+    assert _decode_gqa(**kw) == want
+
+
+def test_decode_gqa_workspace_sizes():
+    # 64 x 32 query heads in groups of 4: 512 workgroups of 4 heads -> split in 4 (at least 256 rows each)
+    assert swa.decode_workspace_bytes(64, 32, 128, 4096, 4, kv_heads=8) == 64 * 32 * 4 * (2 + 128) * 4
+    assert swa.decode_workspace_bytes(64, 32, 128, 4096, 4, kv_heads=32) == 0
+    assert swa.decode_workspace_bytes(64, 32, 128, 4096, 4, kv_heads=5) == 0   # invalid grouping
+    # one key/value head for 8 query heads at batch 1: one job, 16 splits
+    assert swa.decode_workspace_bytes(1, 8, 128, 4096, 4, kv_heads=1) == 8 * 16 * (2 + 128) * 4
