@@ -42,8 +42,10 @@ PREFILL = {
     "gemma3_local_prefill": (1, 16, 131072, 128, 1024, 0, 0.0, 5),
 }
 DECODE = {
-    # name: (batch, heads, d, w, g, pos_lo, pos_hi, seed)
-    "rolling_decode": (64, 32, 128, 4096, 4, 4096, 131072, 4),
+    # name: (batch, heads, kv_heads, d, w, g, pos_lo, pos_hi, seed)
+    "rolling_decode": (64, 32, 32, 128, 4096, 4, 4096, 131072, 4),
+    # grouped-query attention: 4 query heads per key/value head
+    "gqa_decode": (64, 32, 8, 128, 4096, 4, 4096, 131072, 4),
 }
 
 # HBM traffic per launch measured with rocprofv3 counters (FETCH_SIZE and
@@ -155,11 +157,12 @@ def bench_decode(name, steps, warmup):
     import block_sparse_causal_band_amd as swa
     from block_sparse_causal_band_amd import synth
 
-    B, H, d, w, g, lo, hi, seed = DECODE[name]
+    B, H, Hkv, d, w, g, lo, hi, seed = DECODE[name]
     dev = torch.device("cuda")
-    q, kc, vc, pos = synth.decode_problem(B, H, d, g + w, lo, hi, torch.bfloat16, seed=seed, device=dev)
+    q, kc, vc, pos = synth.decode_problem(B, H, d, g + w, lo, hi, torch.bfloat16, seed=seed, device=dev,
+                                          kv_heads=Hkv)
     o = torch.empty_like(q)
-    ws_bytes = swa.decode_workspace_bytes(B, H, d, w, g)
+    ws_bytes = swa.decode_workspace_bytes(B, H, d, w, g, kv_heads=Hkv)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -170,8 +173,9 @@ def bench_decode(name, steps, warmup):
         step()
     torch.cuda.synchronize()
     ms_step, ms_launch, per = _events_time(step, steps, stream)
-    # algorithmic bytes: each query's attended K and V rows once, plus q and o
-    rows = sum(row_pairs(int(p), w, g) for p in pos.cpu().tolist()) * H
+    # algorithmic bytes: each (batch, key/value head)'s attended K and V rows
+    # once (shared by the query heads of its group), plus q and o
+    rows = sum(row_pairs(int(p), w, g) for p in pos.cpu().tolist()) * Hkv
     nbytes = rows * d * 2 * 2 + 2 * B * H * d * 2
     achieved = nbytes / (ms_launch * 1e-3) / 1e9
     traffic = measured_traffic(name, "decode.hip")
@@ -180,7 +184,7 @@ def bench_decode(name, steps, warmup):
         "value": nbytes / (ms_step * 1e-3) / 1e9,
         "unit": "GB/s",
         "dtype": "bf16",
-        "config": {"workload": name, "batch": B, "heads": H, "d": d, "w": w, "g": g,
+        "config": {"workload": name, "batch": B, "heads": H, "kv_heads": Hkv, "d": d, "w": w, "g": g,
                    "positions": [lo, hi], "kv_bytes_per_step": nbytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic, "kernel": "decode_kernel<bf16,128>",
@@ -238,7 +242,7 @@ def cpu_baseline_decode(name, budget_s=10.0):
     import oracle
     from block_sparse_causal_band_amd import synth
 
-    B, H, d, w, g, lo, hi, seed = DECODE[name]
+    B, H, Hkv, d, w, g, lo, hi, seed = DECODE[name]
     orc = oracle.default()
     rng = np.random.default_rng(seed)
     nk = g + w

@@ -62,11 +62,26 @@ __device__ __forceinline__ void unpack(const uint4 &x, float *f) {
     }
 }
 
-// Sum over the kLPR lanes that share one cache row (aligned lane groups).
+// x of another lane through a DPP move (ctrl: quad_perm 0x00-0xff, row
+// mirror 0x140, half-row mirror 0x141); every lane is active where it is used.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the LPR lanes that share one cache row (aligned groups of 8, 16 or
+// 32 lanes).  Within 16 lanes every step is a DPP move: swap neighbours, swap
+// pairs, then the half-row mirror (lane i <- 7-i: quad 0 meets quad 1) and the
+// row mirror (lane i <- 15-i: half 0 meets half 1), each pairing lanes that
+// hold equal partial sums so far.  32 lanes add one cross-row shuffle.
 template <int LPR>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) x += __shfl_xor(x, m, 64);
+    static_assert(LPR == 8 || LPR == 16 || LPR == 32, "row group of 8, 16 or 32 lanes");
+    x += dpp_mov<0xb1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_mov<0x4e>(x);   // quad_perm [2,3,0,1]
+    x += dpp_mov<0x141>(x);
+    if constexpr (LPR >= 16) x += dpp_mov<0x140>(x);
+    if constexpr (LPR >= 32) x += __shfl_xor(x, 16, 64);
     return x;
 }
 
@@ -102,11 +117,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const T *kc = reinterpret_cast<const T *>(kcp) + (size_t)kvu * R * D;
     const T *vc = reinterpret_cast<const T *>(vcp) + (size_t)kvu * R * D;
 
+    // the lane's chunk of each query: fp32 values, and for bf16 also the
+    // packed pairs that the q.k dot2 instructions take as they are
     float qf[GQ][EPC];
+    uint4 qx[GQ];
 #pragma unroll
     for (int j = 0; j < GQ; ++j) {
         const T *q = reinterpret_cast<const T *>(qp) + (size_t)(unit0 + j) * D;
-        unpack<BF16>(*reinterpret_cast<const uint4 *>(q + sub * EPC), qf[j]);
+        qx[j] = *reinterpret_cast<const uint4 *>(q + sub * EPC);
+        if constexpr (!BF16) unpack<BF16>(qx[j], qf[j]);
     }
 
     // ring geometry for this query position
@@ -166,13 +185,21 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                 }
             }
             const float bias = (t < g) ? bias_raw : 0.f;
-            float kf[EPC];
-            unpack<BF16>(kx[u], kf);
 #pragma unroll
             for (int j = 0; j < GQ; ++j) {
                 float acc = 0.f;
+                if constexpr (BF16) {
+                    // bf16 pairs straight from the cache: products exact, fp32 sums
+                    const bf16x2 *k2 = reinterpret_cast<const bf16x2 *>(&kx[u]);
+                    const bf16x2 *q2 = reinterpret_cast<const bf16x2 *>(&qx[j]);
 #pragma unroll
-                for (int e = 0; e < EPC; ++e) acc = fmaf(qf[j][e], kf[e], acc);
+                    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_fdot2_f32_bf16(q2[e], k2[e], acc, false);
+                } else {
+                    float kf[EPC];
+                    unpack<BF16>(kx[u], kf);
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) acc = fmaf(qf[j][e], kf[e], acc);
+                }
                 acc = group_sum<LPR>(acc) + bias;
                 s[j][u] = valid ? acc : kNegInf;
             }
