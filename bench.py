@@ -54,7 +54,13 @@ DECODE = {
 # Each entry records a digest of the kernel source it was measured on; when
 # the source has changed since, the figure no longer describes the kernel and
 # `traffic` is reported as null.
-MEASURED_TRAFFIC = {}
+MEASURED_TRAFFIC = {
+    "mistral_prefill": {"bytes": 1810752641, "source_digest": "aab673279bab0e3e"},
+    "sink_prefill": {"bytes": 5454442202, "source_digest": "aab673279bab0e3e"},
+    "gemma3_local_prefill": {"bytes": 4380782777, "source_digest": "aab673279bab0e3e"},
+    "rolling_decode": {"bytes": 4300235981, "source_digest": "d58ef838d6a89d2b"},
+    "gqa_decode": {"bytes": 1081519983, "source_digest": "d58ef838d6a89d2b"},
+}
 CSRC = os.path.join(ROOT, "block_sparse_causal_band_amd", "csrc")
 
 
