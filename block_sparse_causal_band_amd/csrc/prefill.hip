@@ -292,29 +292,13 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
         if (t + 2 < ntiles) dma(K, dma_k, band.block(t + 2) * kBK, kbuf + cur * L::kTileBytes);
         if (t + 1 < ntiles) dma(V, dma_v, band.block(t + 1) * kBK, vbuf + nxt * L::kTileBytes);
 
-        if constexpr (MASKED) mask_tile(s_cur, qi, k0, lh, n, w, g, bias_raw);
-        update_max(s_cur, m_run, negm, l_run, oacc, c2, tau);
-
-        // The rest of the tile is two interleaved streams, in a fixed order
-        // (sched_barrier pins it; the compiler would otherwise group like
-        // with like, and long runs of MFMAs with no VALU work between them
-        // leave the matrix core and the VALU taking turns):
-        //  A: the score MFMAs of tile t+1, each followed by the exponentials
-        //     of 32/NS scores of tile t (K fragments read 4 MFMAs ahead);
-        //  B: the PV MFMAs of tile t, each group of them preceded by the
-        //     bf16 packing and row-sum dot2s of its probabilities (V^T
-        //     fragments read 3 MFMAs ahead).
-        // On the last tile the A stream reads the other K buffer and its
-        // result is discarded.  The whole stretch runs at raised wave
-        // priority, so when both waves of a SIMD are ready the one feeding
-        // the matrix core issues first.
         const uint8_t *kb = kbuf + nxt * L::kTileBytes;
         const uint8_t *vb = vbuf + cur * L::kTileBytes + voff;
         constexpr int NC = D / 16;       // MFMAs per 32-key score sub-block
         constexpr int NS = 2 * NC;       // score MFMAs per tile
         constexpr int EPS = 32 / NS;     // exponentials per score MFMA
         constexpr int NP = 4 * (D / 32); // PV MFMAs per tile
-        constexpr int KA = 4, VA = 3;    // read-ahead depths
+        constexpr int VA = 3;            // V^T fragment read-ahead
         auto kfrag = [&](int j) -> bf16x8 {
             const int sb = j / NC, c = j % NC;
             const uint32_t off = ((c & 1) ? koff_odd : koff_even) + (c >> 1) * (kBK * 64) + sb * 32 * 64;
@@ -328,21 +312,40 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
             const s16x4 hi = lds_read_tr16(p0 + 8 * 64);
             return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         };
+        // Every K fragment of tile t+1 is read before the mask and the row
+        // max of tile t, whose VALU work then covers the LDS latency.
+        bf16x8 kf[NS];
+#pragma unroll
+        for (int j = 0; j < NS; ++j) kf[j] = kfrag(j);
 
+        if constexpr (MASKED) mask_tile(s_cur, qi, k0, lh, n, w, g, bias_raw);
+        update_max(s_cur, m_run, negm, l_run, oacc, c2, tau);
+
+        // The rest of the tile is two interleaved streams, in a fixed order
+        // (sched_barrier pins it; the compiler would otherwise group like
+        // with like, and long runs of MFMAs with no VALU work between them
+        // leave the matrix core and the VALU taking turns):
+        //  A: the score MFMAs of tile t+1, each followed by the exponentials
+        //     of 32/NS scores of tile t; the first V^T fragments of B are
+        //     read during its last MFMAs;
+        //  B: the PV MFMAs of tile t, each group of them preceded by the
+        //     bf16 packing and row-sum dot2s of its probabilities (V^T
+        //     fragments read 3 MFMAs ahead).
+        // On the last tile the A stream reads the other K buffer and its
+        // result is discarded.  The whole stretch runs at raised wave
+        // priority, so when both waves of a SIMD are ready the one feeding
+        // the matrix core issues first.
         __builtin_amdgcn_s_setprio(1);
         f32x16 s_nxt[2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s_nxt[sb][r] = 0.f;
-        bf16x8 kf[KA];
-#pragma unroll
-        for (int j = 0; j < KA; ++j) kf[j] = kfrag(j);
+        bf16x8 vf[VA];
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-            const bf16x8 a = kf[j % KA];
-            if (j + KA < NS) kf[j % KA] = kfrag(j + KA);
-            s_nxt[j / NC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[j % NC], s_nxt[j / NC], 0, 0, 0);
+            if (j >= NS - VA) vf[j - (NS - VA)] = vfrag(j - (NS - VA));
+            s_nxt[j / NC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j], qf[j % NC], s_nxt[j / NC], 0, 0, 0);
 #pragma unroll
             for (int q = 0; q < EPS; ++q) {
                 const int e = EPS * j + q;
@@ -351,9 +354,6 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
             __builtin_amdgcn_sched_barrier(0);
         }
 
-        bf16x8 vf[VA];
-#pragma unroll
-        for (int j = 0; j < VA; ++j) vf[j] = vfrag(j);
         const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
         float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
