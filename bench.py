@@ -48,6 +48,13 @@ DECODE = {
     "gqa_decode": (64, 32, 8, 128, 4096, 4, 4096, 131072, 4),
 }
 
+CHUNK = {
+    # name: (batch, heads, kv_heads, t, p0, d, w, g, sink_bias, seed): a chunk of t
+    # tokens at positions p0 .. p0+t-1 against a full rolling cache (Mistral 7B's
+    # 32 query / 8 key-value heads and w = 4096, plus 4 sinks)
+    "chunk_prefill": (1, 32, 8, 4096, 16384, 128, 4096, 4, 0.0, 6),
+}
+
 # HBM traffic per launch measured with rocprofv3 counters (FETCH_SIZE and
 # WRITE_SIZE per dispatch, each scaled by what the same counter reads for a
 # plain device copy of known size, see --calibrate-copy), keyed by workload.
@@ -155,6 +162,79 @@ def bench_prefill(name, steps, warmup):
                      "kernel": f"prefill_bf16_kernel<{d},4>" if dtype == torch.bfloat16 else f"prefill_f32_kernel<{d}>",
                      "avg_launch_ms": ms_launch, "min_launch_ms": min(per)},
     }
+
+
+def chunk_pairs(p0: int, t: int, w: int, g: int) -> int:
+    return sum(row_pairs(p0 + i, w, g) for i in range(t))
+
+
+def bench_chunk(name, steps, warmup):
+    import torch
+
+    import block_sparse_causal_band_amd as swa
+    from block_sparse_causal_band_amd import synth
+
+    B, H, Hkv, T, p0, d, w, g, beta, seed = CHUNK[name]
+    dev = torch.device("cuda")
+    q, kn, vn = synth.qkv(B, H, T, d, torch.bfloat16, seed=seed, device=dev, kv_heads=Hkv)
+    kc = synth.normal((B, Hkv, g + w, d), seed=seed + 1, dtype=torch.bfloat16, device=dev)
+    vc = synth.normal((B, Hkv, g + w, d), seed=seed + 2, dtype=torch.bfloat16, device=dev)
+    pos = torch.full((B,), p0, dtype=torch.int64, device=dev)
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        swa.chunk_prefill(q, kn, vn, kc, vc, pos, w=w, g=g, sink_bias=beta, out=o)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ms_step, ms_launch, per = _events_time(step, steps, stream)
+    flops = 4.0 * d * chunk_pairs(p0, T, w, g) * B * H
+    achieved = flops / (ms_launch * 1e-3) / 1e12
+    return {
+        "ms_per_step": ms_step,
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "dtype": "bf16",
+        "config": {"workload": name, "batch": B, "heads": H, "kv_heads": Hkv, "t": T, "p0": p0, "d": d, "w": w,
+                   "g": g, "sink_bias": beta, "band_flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(name, "prefill.hip"),
+                     "kernel": f"prefill_bf16_kernel<{d},4,chunk>",
+                     "avg_launch_ms": ms_launch, "min_launch_ms": min(per)},
+    }
+
+
+def cpu_baseline_chunk(name, budget_s=12.0):
+    """The fp64 oracle on chunk rows of the same workload (each row given the
+    window and sink rows it attends), until about budget_s seconds."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from block_sparse_causal_band_amd import synth
+
+    B, H, Hkv, T, p0, d, w, g, beta, seed = CHUNK[name]
+    orc = oracle.default()
+    units = 32
+    nk = w + g
+    q = synth.normal((units, d), seed=seed, dtype=torch.bfloat16)
+    kk = synth.normal((units, nk, d), seed=seed + 1, dtype=torch.bfloat16)
+    vv = synth.normal((units, nk, d), seed=seed + 2, dtype=torch.bfloat16)
+    rng = np.random.default_rng(seed)
+    done_pairs, done = 0, 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        ps = p0 + rng.integers(0, T, units)
+        kpos = np.stack([np.concatenate([np.arange(p - w + 1, p + 1), np.arange(0, min(g, p - w + 1))]) for p in ps])
+        orc.decode(q, ps, kpos, kk, vv, w=w, g=g, beta=beta)
+        done_pairs += sum(row_pairs(int(p), w, g) for p in ps)
+        done += units
+    dt = time.perf_counter() - t0
+    return {"value": 4.0 * d * done_pairs / dt / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(),
+            "kind": "oracle", "sample": f"{done} chunk rows of {name} (random rows, each with its {nk} attended keys), "
+                                        f"fp64, {dt:.1f} s"}
 
 
 def bench_decode(name, steps, warmup):
@@ -299,7 +379,7 @@ def main():
     # the clock settles over the first ~25 launches of a busy kernel (power
     # management); the default warmup keeps the timed launches past that
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="mistral_prefill", choices=sorted(PREFILL) + sorted(DECODE))
+    ap.add_argument("--workload", default="mistral_prefill", choices=sorted(PREFILL) + sorted(DECODE) + sorted(CHUNK))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode figures on a prefill line")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -321,6 +401,8 @@ def main():
 
     if args.workload in PREFILL:
         r = bench_prefill(args.workload, args.steps, args.warmup)
+    elif args.workload in CHUNK:
+        r = bench_chunk(args.workload, args.steps, args.warmup)
     else:
         r = bench_decode(args.workload, args.steps, args.warmup)
     line = {
@@ -348,6 +430,8 @@ def main():
     if not args.no_cpu_baseline:
         if args.workload in PREFILL:
             line["cpu_baseline"] = cpu_baseline_prefill(args.workload)
+        elif args.workload in CHUNK:
+            line["cpu_baseline"] = cpu_baseline_chunk(args.workload)
         else:
             line["cpu_baseline"] = cpu_baseline_decode(args.workload)
     print(json.dumps(line), flush=True)

@@ -4,6 +4,7 @@ The computation lives in libswa.so (hand-written HIP kernels for gfx950
 behind the C ABI of include/swa.h); this package is its thin Python binding.
 
     from block_sparse_causal_band_amd import prefill, kv_append, decode
+    from block_sparse_causal_band_amd import chunk_prefill, lse_merge
 
 Importing the package does not load the library; the first call does, and
 raises if it is not built (``python -m block_sparse_causal_band_amd.build``).
@@ -13,10 +14,12 @@ from .binding import (  # noqa: F401
     SWA_F32,
     SwaError,
     band_tiles,
+    chunk_prefill,
     decode,
     decode_workspace_bytes,
     kv_append,
     lib,
+    lse_merge,
     prefill,
     prefill_order,
     prefill_tile_shape,

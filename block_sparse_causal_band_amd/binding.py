@@ -62,6 +62,10 @@ def lib() -> ctypes.CDLL:
         L.swa_decode_fwd_gqa.restype = _int
         L.swa_decode_workspace_bytes_gqa.argtypes = [_int] * 6
         L.swa_decode_workspace_bytes_gqa.restype = ctypes.c_size_t
+        L.swa_chunk_prefill_fwd.argtypes = [_vp] * 8 + [_int] * 7 + [ctypes.c_float] * 2 + [_int, _int, _vp]
+        L.swa_chunk_prefill_fwd.restype = _int
+        L.swa_lse_merge.argtypes = [_vp] * 6 + [ctypes.c_longlong, _int, _int, _vp]
+        L.swa_lse_merge.restype = _int
         L.swa_strerror.argtypes = [_int]
         L.swa_strerror.restype = ctypes.c_char_p
         L.swa_band_tiles.argtypes = [_int, _int, _int, _int, _int, _vp, ctypes.c_long]
@@ -196,6 +200,66 @@ def decode(q, k_cache, v_cache, pos, w: int, g: int = 0, scale: float | None = N
                                   _stream(q))
     if rc != 0:
         raise SwaError(rc, "swa_decode_fwd_gqa")
+    return (o, lse) if return_lse else o
+
+
+KEYS = {"all": 0, "cache": 1, "chunk": 2}
+
+
+def chunk_prefill(q, k_new, v_new, k_cache, v_cache, pos, w: int, g: int = 0, scale: float | None = None,
+                  sink_bias: float = 0.0, keys: str = "all", return_lse: bool = False, out=None):
+    """Chunked prefill against the rolling cache: q [batch, heads, t, d] at
+    positions pos[b] .. pos[b]+t-1, the chunk's own k_new, v_new [batch,
+    kv_heads, t, d] and caches [batch, kv_heads, g + w, d] holding positions
+    < pos[b].  keys: "all", or the partial over "cache" or "chunk" keys."""
+    import torch
+
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("pos", pos)):
+        _dev_tensor(t, name)
+    _need(q.dim() == 4 and k_new.dim() == 4 and k_new.shape == v_new.shape, "q, k_new, v_new must be 4-d")
+    B, H, t, d = q.shape
+    Hkv = k_new.shape[1]
+    _need(k_new.shape == (B, Hkv, t, d), "k_new, v_new must be [batch, kv_heads, t, d]")
+    _need(k_cache.shape == v_cache.shape == (B, Hkv, g + w, d), "caches must be [batch, kv_heads, g + w, d]")
+    _need(q.dtype == k_new.dtype == v_new.dtype == k_cache.dtype == v_cache.dtype, "one dtype for every tensor")
+    _need(pos.dtype == torch.int64 and pos.shape == (B,), "pos must be int64 [batch]")
+    _need(keys in KEYS, "keys must be 'all', 'cache' or 'chunk'")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    _dev_tensor(o, "out")
+    _need(o.shape == q.shape and o.dtype == q.dtype, "out must match q")
+    lse = torch.empty((B, H, t), dtype=torch.float32, device=q.device) if return_lse else None
+    rc = lib().swa_chunk_prefill_fwd(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
+                                     v_cache.data_ptr(), pos.data_ptr(), o.data_ptr(),
+                                     lse.data_ptr() if lse is not None else None, B, H, Hkv, t, d, int(w), int(g),
+                                     float(scale), float(sink_bias), KEYS[keys], _dtype_code(q), _stream(q))
+    if rc != 0:
+        raise SwaError(rc, "swa_chunk_prefill_fwd")
+    return (o, lse) if return_lse else o
+
+
+def lse_merge(o_a, lse_a, o_b, lse_b, return_lse: bool = True, out=None):
+    """Merge two partial attentions of the same rows over disjoint key sets:
+    o_* [..., d] with lse_* [...] fp32."""
+    import torch
+
+    for name, t in (("o_a", o_a), ("lse_a", lse_a), ("o_b", o_b), ("lse_b", lse_b)):
+        _dev_tensor(t, name)
+    _need(o_a.shape == o_b.shape and o_a.dtype == o_b.dtype, "o_a and o_b must match")
+    _need(lse_a.shape == lse_b.shape == o_a.shape[:-1], "lse_a, lse_b must be o's shape without d")
+    _need(lse_a.dtype == lse_b.dtype == torch.float32, "lse must be fp32")
+    d = o_a.shape[-1]
+    rows = o_a.numel() // d
+    o = torch.empty_like(o_a) if out is None else out
+    _dev_tensor(o, "out")
+    _need(o.shape == o_a.shape and o.dtype == o_a.dtype, "out must match o_a")
+    lse = torch.empty_like(lse_a) if return_lse else None
+    rc = lib().swa_lse_merge(o_a.data_ptr(), lse_a.data_ptr(), o_b.data_ptr(), lse_b.data_ptr(), o.data_ptr(),
+                             lse.data_ptr() if lse is not None else None, rows, d, _dtype_code(o_a), _stream(o_a))
+    if rc != 0:
+        raise SwaError(rc, "swa_lse_merge")
     return (o, lse) if return_lse else o
 
 

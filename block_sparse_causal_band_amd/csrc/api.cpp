@@ -19,6 +19,12 @@ hipError_t launch_decode(const void *q, const void *kc, const void *vc, const in
 hipError_t launch_kv_append(void *kc, void *vc, const void *kn, const void *vn, const int64_t *pos, int batch,
                             int heads, int tn, int d, int w, int g, bool bf16, hipStream_t stream);
 size_t decode_workspace_bytes(int batch, int heads, int kv_heads, int d, int rows);
+hipError_t launch_chunk_prefill(const void *q, const void *k_new, const void *v_new, const void *k_cache,
+                                const void *v_cache, const int64_t *pos, void *o, float *lse, int batch, int heads,
+                                int kv_heads, int t, int d, int w, int g, float scale, float sink_bias, int part,
+                                bool bf16, hipStream_t stream);
+hipError_t launch_lse_merge(const void *oa, const float *la, const void *ob, const float *lb, void *o, float *lse,
+                            long rows, int d, bool bf16, hipStream_t stream);
 int prefill_rows_per_workgroup(bool bf16);
 // keys per prefill tile (prefill.hip)
 constexpr int kPrefillBK = 64;
@@ -94,6 +100,47 @@ int swa_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v
     if (blocks > INT_MAX) return SWA_EINVAL;
     return status_of(swa::launch_kv_append(k_cache, v_cache, k_new, v_new, pos, batch, heads, t_new, d, w, g,
                                            dtype == SWA_BF16, stream));
+}
+
+int swa_chunk_prefill_fwd(const void *q, const void *k_new, const void *v_new, const void *k_cache,
+                          const void *v_cache, const int64_t *pos, void *o, float *lse, int batch, int heads,
+                          int kv_heads, int t, int d, int w, int g, float scale, float sink_bias, int keys,
+                          swa_dtype_t dtype, hipStream_t stream) {
+    if (!q || !k_new || !v_new || !k_cache || !v_cache || !pos || !o) return SWA_EINVAL;
+    if (batch < 1 || heads < 1 || t < 1 || w < 1 || g < 0) return SWA_EINVAL;
+    if (kv_heads < 1 || kv_heads > heads || heads % kv_heads != 0) return SWA_EINVAL;
+    if (keys != SWA_KEYS_ALL && keys != SWA_KEYS_CACHE && keys != SWA_KEYS_CHUNK) return SWA_EINVAL;
+    if ((long long)g + w > INT_MAX / 2) return SWA_EINVAL;
+    if (!std::isfinite(scale) || !(scale > 0.f) || !std::isfinite(sink_bias)) return SWA_EINVAL;
+    int st = check_dtype_d(dtype, d);
+    if (st != SWA_OK) return st;
+    const int bq = swa::prefill_bq(dtype == SWA_BF16);
+    if (t > INT_MAX - bq) return SWA_EINVAL;
+    const long long units = (long long)batch * heads;
+    const long long nqb = (t + bq - 1) / bq;
+    if (units * nqb > INT_MAX) return SWA_EINVAL;
+    // byte offsets of one (batch, head)'s rows stay below 2^32 for the buffer loads
+    const long long row_bytes = (long long)d * (dtype == SWA_BF16 ? 2 : 4);
+    if ((long long)t * row_bytes >= (1LL << 32) || ((long long)g + w) * row_bytes >= (1LL << 32)) return SWA_EINVAL;
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        !aligned16(o) || (reinterpret_cast<uintptr_t>(pos) & 7u) || (lse && !aligned4(lse)))
+        return SWA_EALIGN;
+    return status_of(swa::launch_chunk_prefill(q, k_new, v_new, k_cache, v_cache, pos, o, lse, batch, heads,
+                                               kv_heads, t, d, w, g, scale, sink_bias, keys, dtype == SWA_BF16,
+                                               stream));
+}
+
+int swa_lse_merge(const void *o_a, const float *lse_a, const void *o_b, const float *lse_b, void *o, float *lse,
+                  long long rows, int d, swa_dtype_t dtype, hipStream_t stream) {
+    if (!o_a || !lse_a || !o_b || !lse_b || !o) return SWA_EINVAL;
+    if (rows < 1) return SWA_EINVAL;
+    int st = check_dtype_d(dtype, d);
+    if (st != SWA_OK) return st;
+    if (rows * (d / 4) / 256 + 1 > INT_MAX) return SWA_EINVAL;
+    if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o) || !aligned4(lse_a) || !aligned4(lse_b) ||
+        (lse && !aligned4(lse)))
+        return SWA_EALIGN;
+    return status_of(swa::launch_lse_merge(o_a, lse_a, o_b, lse_b, o, lse, (long)rows, d, dtype == SWA_BF16, stream));
 }
 
 size_t swa_decode_workspace_bytes_gqa(int batch, int heads, int kv_heads, int d, int w, int g) {

@@ -75,6 +75,28 @@ __device__ __forceinline__ size_t kv_offset(int unit, int heads, int kv_heads, i
     return ((size_t)b * kv_heads + h / (heads / kv_heads)) * n * d;
 }
 
+// Chunked prefill against the rolling cache: the queries of a chunk are the
+// positions p0 .. p0+T-1 of batch entry b (p0 = pos[b]); a key position s >=
+// p0 is row s-p0 of the chunk's own K/V, a key position s < p0 is in the
+// cache: ring row g + s mod w while s >= p0-w (the ring still holds it), else
+// sink row s ("Sliding Window and Sparse Attention, from Longformer to CSA2",
+// s2: rolling buffer, sinks; "Local and Sparse Attention: Reading Fewer Token
+// Positions", Figure 4: circular overwrite, kept anchors).  Positions that are
+// neither were evicted and are never attended; their loads land on some
+// finite cache row or read as zero past the cache and are masked.
+// part: 0 = every key, 1 = cache keys only (s < p0), 2 = chunk keys only.
+struct ChunkArgs {
+    const void *kc;        // K cache [batch][kv_heads][g + w][d]
+    const void *vc;        // V cache, same layout
+    const int64_t *pos;    // p0 of each batch entry
+    int part;
+};
+
+// Cache row of key position s < p0 (s >= 0).
+__device__ __forceinline__ int cache_row(int s, int p0, int w, int g) {
+    return (s >= p0 - w) ? g + s % w : s;
+}
+
 // ---------------------------------------------------------------------------
 // Pieces shared by both paths.  s[sb][r] holds q_qi . k_j for the key
 // j = k0 + 32 sb + 8 (r/4) + 4 lh + r%4 (the 32x32 MFMA result layout).
@@ -82,10 +104,12 @@ __device__ __forceinline__ size_t kv_offset(int unit, int heads, int kv_heads, i
 // Exact predicate on a cut tile.  A tile whose keys are all >= g and < n is
 // cut only by the window and causality: 0 <= qi - j < w, one unsigned compare
 // per score.  Tiles with sink keys or past the end of the sequence take the
-// full predicate and the sink bias.
+// full predicate and the sink bias.  KLO: keys below klo are excluded too
+// (a partial attention over the keys >= klo only).
+template <bool KLO = false>
 __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int qi, int k0, int lh, int n, int w, int g,
-                                          float bias_raw) {
-    if (k0 >= g && k0 + kBK <= n) {
+                                          float bias_raw, int klo = 0) {
+    if (k0 >= g && k0 + kBK <= n && (!KLO || k0 >= klo)) {
         const int diff = qi - k0 - 4 * lh;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
@@ -102,7 +126,7 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int qi, int k0, int lh
         for (int r = 0; r < 16; ++r) {
             const int j = k0 + 32 * sb + 8 * (r >> 2) + 4 * lh + (r & 3);
             const float x = s[sb][r] + (j < g ? bias_raw : 0.f);
-            s[sb][r] = pair_attended(qi, j, n, w, g) ? x : kNegInf;
+            s[sb][r] = (pair_attended(qi, j, n, w, g) && (!KLO || j >= klo)) ? x : kNegInf;
         }
 }
 
@@ -174,11 +198,14 @@ struct Bf16Tile {
     }
 };
 
-template <int D, int WAVES>
+// CHUNK: the queries are a chunk of n positions starting at p0 = pos[b] and
+// the keys come from the chunk and the cache (ChunkArgs); otherwise q, k, v
+// are whole sequences of n positions and p0 = 0.
+template <int D, int WAVES, bool CHUNK>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp, const uint16_t *__restrict__ vp,
     uint16_t *__restrict__ op, float *__restrict__ lsep, int n, int nqb, int w, int g, float c2, float scale,
-    float bias_raw, int total_wg, int heads, int kv_heads) {
+    float bias_raw, int total_wg, int heads, int kv_heads, ChunkArgs ca) {
     using L = Bf16Tile<D, WAVES>;
     constexpr int BQ = 32 * WAVES;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * L::kStageBytes];
@@ -196,10 +223,34 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     const uint16_t *K = kp + kv_offset(unit, heads, kv_heads, n, D);
     const uint16_t *V = vp + kv_offset(unit, heads, kv_heads, n, D);
 
-    const int q0 = qb * BQ;
+    const int q0 = qb * BQ;  // rows of this block: q0 .. q1 (< n)
     const int q1 = min(q0 + BQ, n) - 1;
     const int qi = q0 + wave * 32 + lr;
-    const BandRange band = band_range(q0, q1, w, g, kBK);
+    // positions: query row r is at p0 + r; keys are attended in [klo, khi)
+    int p0 = 0, klo = 0, khi = n;
+    const uint16_t *KC = nullptr, *VC = nullptr;
+    if constexpr (CHUNK) {
+        const int b = unit / heads;
+        const int64_t pb = ca.pos[b];
+        if (pb < 0 || pb > (int64_t)(0x7fffffff - n)) {
+            // no valid position: the rows are NaN
+            if (qi < n) {
+                uint16_t *orow = op + base + (size_t)qi * D;
+                for (int c = 4 * lh; c < D; c += 8)
+                    *reinterpret_cast<uint2 *>(orow + c) = make_uint2(0x7fc07fc0u, 0x7fc07fc0u);
+                if (lsep != nullptr && lh == 0) lsep[(size_t)unit * n + qi] = __builtin_nanf("");
+            }
+            return;
+        }
+        p0 = (int)pb;
+        klo = (ca.part == 2) ? p0 : 0;
+        khi = (ca.part == 1) ? p0 : p0 + n;
+        const size_t coff = kv_offset(unit, heads, kv_heads, g + w, D);
+        KC = reinterpret_cast<const uint16_t *>(ca.kc) + coff;
+        VC = reinterpret_cast<const uint16_t *>(ca.vc) + coff;
+    }
+    const int qa = p0 + qi;  // position of this lane's query row
+    const BandRange band = band_range(p0 + q0, p0 + q1, w, g, kBK);
     const int ntiles = band.count();
     const float tau = 8.f / c2;
 
@@ -232,10 +283,41 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     }
     uint8_t *const kbuf = smem;                       // K buffers 0, 1
     uint8_t *const vbuf = smem + 2 * L::kTileBytes;   // V buffers 0, 1
-    auto dma = [&](const uint16_t *src, const uint32_t *offs, int k0, uint8_t *dst) {
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)k0 * D, (uint32_t)(n - k0) * L::kRowBytes);
+    auto dma_rows = [&](const uint16_t *src, const uint32_t *offs, int r0, int nrows, uint8_t *dst) {
+        // rows r0 .. of src, rows >= nrows read as zero
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)r0 * D, (uint32_t)(nrows - r0) * L::kRowBytes);
 #pragma unroll
         for (int i = 0; i < L::kDmaPerWave; ++i) dma16(r, dst + (wave * L::kDmaPerWave + i) * 1024, offs[i]);
+    };
+    // tile of key positions k0 .. k0+63 of K (or V) into LDS at dst
+    auto dma = [&](bool is_k, int k0, uint8_t *dst) {
+        const uint16_t *src = is_k ? K : V;
+        const uint32_t *offs = is_k ? dma_k : dma_v;
+        if constexpr (!CHUNK) {
+            dma_rows(src, offs, k0, n, dst);
+        } else {
+            const uint16_t *cache = is_k ? KC : VC;
+            if (k0 >= p0) {
+                dma_rows(src, offs, k0 - p0, n, dst);  // all in the chunk
+            } else if (k0 + kBK <= p0 && k0 >= p0 - w && k0 % w + kBK <= w) {
+                dma_rows(cache, offs, g + k0 % w, g + w, dst);  // one unwrapped run of the ring
+            } else {
+                // row by row: chunk, ring or sink row of each key position
+                const __amdgpu_buffer_rsrc_t rn = make_rsrc(src, (uint32_t)n * L::kRowBytes);
+                const __amdgpu_buffer_rsrc_t rc = make_rsrc(cache, (uint32_t)(g + w) * L::kRowBytes);
+#pragma unroll
+                for (int i = 0; i < L::kDmaPerWave; ++i) {
+                    const int key = (int)(offs[i] / L::kRowBytes);
+                    const uint32_t part = offs[i] - (uint32_t)key * L::kRowBytes;
+                    const int sp = k0 + key;
+                    uint8_t *d = dst + (wave * L::kDmaPerWave + i) * 1024;
+                    if (sp >= p0)
+                        dma16(rn, d, (uint32_t)(sp - p0) * L::kRowBytes + part);
+                    else
+                        dma16(rc, d, (uint32_t)cache_row(sp, p0, w, g) * L::kRowBytes + part);
+                }
+            }
+        }
     };
 
     // Per-lane LDS read offsets within a buffer.
@@ -276,9 +358,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     // computes the scores of tile t+1.  During tile t the DMA fills K(t+2) into
     // the K buffer that K(t) left and V(t+1) into the V buffer that V(t-1)
     // left, so every DMA has a whole tile of time to land.
-    dma(K, dma_k, band.block(0) * kBK, kbuf);
-    dma(V, dma_v, band.block(0) * kBK, vbuf);
-    if (ntiles > 1) dma(K, dma_k, band.block(1) * kBK, kbuf + L::kTileBytes);
+    dma(true, band.block(0) * kBK, kbuf);
+    dma(false, band.block(0) * kBK, vbuf);
+    if (ntiles > 1) dma(true, band.block(1) * kBK, kbuf + L::kTileBytes);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     f32x16 s_cur[2];
@@ -289,8 +371,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
         constexpr bool MASKED = decltype(masked_tag)::value;
         const int cur = t & 1, nxt = cur ^ 1;
         const int k0 = band.block(t) * kBK;
-        if (t + 2 < ntiles) dma(K, dma_k, band.block(t + 2) * kBK, kbuf + cur * L::kTileBytes);
-        if (t + 1 < ntiles) dma(V, dma_v, band.block(t + 1) * kBK, vbuf + nxt * L::kTileBytes);
+        if (t + 2 < ntiles) dma(true, band.block(t + 2) * kBK, kbuf + cur * L::kTileBytes);
+        if (t + 1 < ntiles) dma(false, band.block(t + 1) * kBK, vbuf + nxt * L::kTileBytes);
 
         const uint8_t *kb = kbuf + nxt * L::kTileBytes;
         const uint8_t *vb = vbuf + cur * L::kTileBytes + voff;
@@ -318,7 +400,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
 #pragma unroll
         for (int j = 0; j < NS; ++j) kf[j] = kfrag(j);
 
-        if constexpr (MASKED) mask_tile(s_cur, qi, k0, lh, n, w, g, bias_raw);
+        if constexpr (MASKED) mask_tile<CHUNK>(s_cur, qa, k0, lh, khi, w, g, bias_raw, klo);
         update_max(s_cur, m_run, negm, l_run, oacc, c2, tau);
 
         // The rest of the tile is two interleaved streams, in a fixed order
@@ -390,7 +472,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     // workgroup's block cut a single wave's rows in fewer tiles.
     int t_lo = 0, t_hi = ntiles;  // a wave entirely past n keeps all tiles unmasked (nothing is stored)
     const int qw0 = q0 + wave * 32;
-    if (qw0 < n) full_range(band, qw0, min(qw0 + 31, n - 1), n, w, g, kBK, &t_lo, &t_hi);
+    if (qw0 < n) full_range(band, p0 + qw0, p0 + min(qw0 + 31, n - 1), khi, w, g, kBK, &t_lo, &t_hi, klo);
     int t = 0;
     for (; t < t_lo; ++t) do_tile(t, std::true_type{});
     for (; t < t_hi; ++t) do_tile(t, std::false_type{});
@@ -415,27 +497,41 @@ struct F32Cfg {
     static_assert(kBK * kCPR % kThreads == 0 && (kBK / 4) * kCPR % kThreads == 0, "tile split");
 };
 
+// Where the fp32 loader finds key position s: whole-sequence rows (p0 = 0,
+// rows >= n read as zero), or chunk / cache rows as in the bf16 path.
+struct F32KeyRows {
+    const float *k, *v;    // sequence or chunk rows
+    const float *kc, *vc;  // cache rows (chunked prefill only)
+    int n, p0, w, g;
+    bool chunk;
+    __device__ __forceinline__ uint4 load(bool is_k, int s, int col_byte, int d) const {
+        if (!chunk || s >= p0) {
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(is_k ? k : v, (uint32_t)n * d * 4);
+            return buffer_load16(r, (uint32_t)(s - p0) * d * 4 + col_byte);
+        }
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(is_k ? kc : vc, (uint32_t)(g + w) * d * 4);
+        return buffer_load16(r, (uint32_t)cache_row(s, p0, w, g) * d * 4 + col_byte);
+    }
+};
+
 template <int D>
 struct F32TileLoader {
     using C = F32Cfg<D>;
     uint4 k[C::kKChunks];
     uint4 v[C::kVBlocks][4];
 
-    __device__ __forceinline__ void load(const float *kb, const float *vb, int k0, int n, int tid) {
-        const uint32_t bytes = (uint32_t)(n - k0) * D * 4;
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + (size_t)k0 * D, bytes);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + (size_t)k0 * D, bytes);
+    __device__ __forceinline__ void load(const F32KeyRows &src, int k0, int tid) {
 #pragma unroll
         for (int i = 0; i < C::kKChunks; ++i) {
             const int id = tid + kThreads * i;
-            k[i] = buffer_load16(rk, (id / C::kCPR) * D * 4 + (id % C::kCPR) * 16);
+            k[i] = src.load(true, k0 + id / C::kCPR, (id % C::kCPR) * 16, D);
         }
 #pragma unroll
         for (int i = 0; i < C::kVBlocks; ++i) {
             const int id = tid + kThreads * i;
             const int kg = id % (kBK / 4), cg = id / (kBK / 4);
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) v[i][rr] = buffer_load16(rv, (4 * kg + rr) * D * 4 + cg * 16);
+            for (int rr = 0; rr < 4; ++rr) v[i][rr] = src.load(false, k0 + 4 * kg + rr, cg * 16, D);
         }
     }
     __device__ __forceinline__ void store(float *ks, float *vts, int tid) const {
@@ -460,11 +556,11 @@ struct F32TileLoader {
     }
 };
 
-template <int D>
+template <int D, bool CHUNK>
 __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
     const float *__restrict__ qp, const float *__restrict__ kp, const float *__restrict__ vp,
     float *__restrict__ op, float *__restrict__ lsep, int n, int nqb, int w, int g, float c2, float scale,
-    float bias_raw, int total_wg, int heads, int kv_heads) {
+    float bias_raw, int total_wg, int heads, int kv_heads, ChunkArgs ca) {
     using C = F32Cfg<D>;
     __shared__ __attribute__((aligned(16))) float smem[2 * C::kStage];
 
@@ -484,7 +580,32 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
     const int q0 = qb * kBQ;
     const int q1 = min(q0 + kBQ, n) - 1;
     const int qi = q0 + wave * 32 + lr;
-    const BandRange band = band_range(q0, q1, w, g, kBK);
+    F32KeyRows src{K, V, nullptr, nullptr, n, 0, w, g, CHUNK};
+    int p0 = 0, klo = 0, khi = n;
+    if constexpr (CHUNK) {
+        const int b = unit / heads;
+        const int64_t pb = ca.pos[b];
+        if (pb < 0 || pb > (int64_t)(0x7fffffff - n)) {
+            if (qi < n) {
+                float *orow = op + base + (size_t)qi * D;
+                for (int c = 4 * lh; c < D; c += 8) {
+                    const float nan = __builtin_nanf("");
+                    *reinterpret_cast<float4 *>(orow + c) = make_float4(nan, nan, nan, nan);
+                }
+                if (lsep != nullptr && lh == 0) lsep[(size_t)unit * n + qi] = __builtin_nanf("");
+            }
+            return;
+        }
+        p0 = (int)pb;
+        klo = (ca.part == 2) ? p0 : 0;
+        khi = (ca.part == 1) ? p0 : p0 + n;
+        const size_t coff = kv_offset(unit, heads, kv_heads, g + w, D);
+        src.kc = reinterpret_cast<const float *>(ca.kc) + coff;
+        src.vc = reinterpret_cast<const float *>(ca.vc) + coff;
+        src.p0 = p0;
+    }
+    const int qa = p0 + qi;
+    const BandRange band = band_range(p0 + q0, p0 + q1, w, g, kBK);
     const int ntiles = band.count();
     const float tau = 8.f / c2;
 
@@ -511,7 +632,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
     float m_run = kNegInf, negm = 0.f, l_run = 0.f;
 
     F32TileLoader<D> ld;
-    ld.load(K, V, band.block(0) * kBK, n, tid);
+    ld.load(src, band.block(0) * kBK, tid);
     ld.store(smem, smem + C::kKElems, tid);
     __syncthreads();
 
@@ -521,7 +642,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
         const float *Vts = Ks + C::kKElems;
         const int k0 = band.block(t) * kBK;
         const bool has_next = (t + 1 < ntiles);
-        if (has_next) ld.load(K, V, band.block(t + 1) * kBK, n, tid);
+        if (has_next) ld.load(src, band.block(t + 1) * kBK, tid);
 
         f32x16 s[2];
 #pragma unroll
@@ -533,7 +654,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
             for (int c = 0; c < D / 2; ++c)
                 s[sb] = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * c], qf[c], s[sb], 0, 0, 0);
         }
-        if constexpr (MASKED) mask_tile(s, qi, k0, lh, n, w, g, bias_raw);
+        if constexpr (MASKED) mask_tile<CHUNK>(s, qa, k0, lh, khi, w, g, bias_raw, klo);
         update_max(s, m_run, negm, l_run, oacc, c2, tau);
 
         float lsum = 0.f;
@@ -564,7 +685,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
     };
 
     int t_lo, t_hi;
-    full_range(band, q0, q1, n, w, g, kBK, &t_lo, &t_hi);
+    full_range(band, p0 + q0, p0 + q1, khi, w, g, kBK, &t_lo, &t_hi, klo);
     int t = 0, stage = 0;
     for (; t < t_lo; ++t, stage ^= 1) do_tile(t, stage, std::true_type{});
     for (; t < t_hi; ++t, stage ^= 1) do_tile(t, stage, std::false_type{});
@@ -577,10 +698,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
 // Query rows per workgroup (the prefill grid is units x ceil(n / rows)).
 int prefill_rows_per_workgroup(bool bf16) { return bf16 ? 32 * kWaves16 : kBQ; }
 
-// Host launcher (validated arguments only).
-hipError_t launch_prefill(const void *q, const void *k, const void *v, void *o, float *lse, int batch, int heads,
-                          int kv_heads, int n, int d, int w, int g, float scale, float sink_bias, bool bf16,
-                          hipStream_t stream) {
+// Host launchers (validated arguments only).
+template <bool CHUNK>
+static hipError_t launch_prefill_t(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
+                                   int heads, int kv_heads, int n, int d, int w, int g, float scale,
+                                   float sink_bias, bool bf16, ChunkArgs ca, hipStream_t stream) {
     const int units = batch * heads;
     const float c2 = (float)((double)scale * kLog2e);
     const float bias_raw = (float)((double)sink_bias / (double)scale);
@@ -592,11 +714,11 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, void *o, 
         const uint16_t *qq = (const uint16_t *)q, *kk = (const uint16_t *)k, *vv = (const uint16_t *)v;
         uint16_t *oo = (uint16_t *)o;
         if (d == 128)
-            hipLaunchKernelGGL((prefill_bf16_kernel<128, kWaves16>), grid, block, 0, stream, qq, kk, vv, oo, lse, n,
-                               nqb, w, g, c2, scale, bias_raw, total, heads, kv_heads);
+            hipLaunchKernelGGL((prefill_bf16_kernel<128, kWaves16, CHUNK>), grid, block, 0, stream, qq, kk, vv, oo,
+                               lse, n, nqb, w, g, c2, scale, bias_raw, total, heads, kv_heads, ca);
         else
-            hipLaunchKernelGGL((prefill_bf16_kernel<64, kWaves16>), grid, block, 0, stream, qq, kk, vv, oo, lse, n,
-                               nqb, w, g, c2, scale, bias_raw, total, heads, kv_heads);
+            hipLaunchKernelGGL((prefill_bf16_kernel<64, kWaves16, CHUNK>), grid, block, 0, stream, qq, kk, vv, oo,
+                               lse, n, nqb, w, g, c2, scale, bias_raw, total, heads, kv_heads, ca);
     } else {
         const int nqb = (n + kBQ - 1) / kBQ;
         const int total = units * nqb;
@@ -604,12 +726,89 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, void *o, 
         const float *qq = (const float *)q, *kk = (const float *)k, *vv = (const float *)v;
         float *oo = (float *)o;
         if (d == 128)
-            hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, block, 0, stream, qq, kk, vv, oo, lse, n, nqb, w, g, c2,
-                               scale, bias_raw, total, heads, kv_heads);
+            hipLaunchKernelGGL((prefill_f32_kernel<128, CHUNK>), grid, block, 0, stream, qq, kk, vv, oo, lse, n, nqb,
+                               w, g, c2, scale, bias_raw, total, heads, kv_heads, ca);
         else
-            hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, block, 0, stream, qq, kk, vv, oo, lse, n, nqb, w, g, c2,
-                               scale, bias_raw, total, heads, kv_heads);
+            hipLaunchKernelGGL((prefill_f32_kernel<64, CHUNK>), grid, block, 0, stream, qq, kk, vv, oo, lse, n, nqb,
+                               w, g, c2, scale, bias_raw, total, heads, kv_heads, ca);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill(const void *q, const void *k, const void *v, void *o, float *lse, int batch, int heads,
+                          int kv_heads, int n, int d, int w, int g, float scale, float sink_bias, bool bf16,
+                          hipStream_t stream) {
+    return launch_prefill_t<false>(q, k, v, o, lse, batch, heads, kv_heads, n, d, w, g, scale, sink_bias, bf16,
+                                   ChunkArgs{nullptr, nullptr, nullptr, 0}, stream);
+}
+
+hipError_t launch_chunk_prefill(const void *q, const void *k_new, const void *v_new, const void *k_cache,
+                                const void *v_cache, const int64_t *pos, void *o, float *lse, int batch, int heads,
+                                int kv_heads, int t, int d, int w, int g, float scale, float sink_bias, int part,
+                                bool bf16, hipStream_t stream) {
+    return launch_prefill_t<true>(q, k_new, v_new, o, lse, batch, heads, kv_heads, t, d, w, g, scale, sink_bias,
+                                  bf16, ChunkArgs{k_cache, v_cache, pos, part}, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Log-sum-exp merge of two partial attentions over disjoint key sets of the
+// same query rows ("Sliding Window and Sparse Attention, from Longformer to
+// CSA2", s10 glossary, LSE): with M = max(lse_a, lse_b),
+//   o = (e^(lse_a - M) o_a + e^(lse_b - M) o_b) / (e^(lse_a - M) + e^(lse_b - M)),
+//   lse = M + ln(e^(lse_a - M) + e^(lse_b - M)).
+// A part with lse = -inf (no key) has weight 0; two empty parts give o = 0
+// and lse = -inf.  One thread per 4 columns of a row.
+template <typename T>
+__global__ __launch_bounds__(256) void lse_merge_kernel(const T *__restrict__ oa, const float *__restrict__ la,
+                                                       const T *__restrict__ ob, const float *__restrict__ lb,
+                                                       T *__restrict__ o, float *__restrict__ lse, long rows,
+                                                       int d) {
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    const int per_row = d / 4;
+    const long row = idx / per_row;
+    if (row >= rows) return;
+    const int c = (int)(idx - row * per_row) * 4;
+    const float a = la[row], b = lb[row];
+    const float M = fmaxf(a, b);
+    float wa = 0.f, wb = 0.f;
+    if (M != kNegInf) {
+        wa = fast_exp2((a - M) * (float)kLog2e);
+        wb = fast_exp2((b - M) * (float)kLog2e);
+    }
+    const float sum = wa + wb;
+    const float inv = (sum > 0.f) ? 1.f / sum : 0.f;
+    wa *= inv;
+    wb *= inv;
+    float xa[4], xb[4];
+    const size_t off = (size_t)row * d + c;
+    if constexpr (std::is_same<T, uint16_t>::value) {
+        const uint2 ua = *reinterpret_cast<const uint2 *>(oa + off), ub = *reinterpret_cast<const uint2 *>(ob + off);
+        xa[0] = bf16lo(ua.x); xa[1] = bf16hi(ua.x); xa[2] = bf16lo(ua.y); xa[3] = bf16hi(ua.y);
+        xb[0] = bf16lo(ub.x); xb[1] = bf16hi(ub.x); xb[2] = bf16lo(ub.y); xb[3] = bf16hi(ub.y);
+        float r[4];
+        for (int e = 0; e < 4; ++e) r[e] = (wa > 0.f ? wa * xa[e] : 0.f) + (wb > 0.f ? wb * xb[e] : 0.f);
+        *reinterpret_cast<uint2 *>(o + off) = make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
+    } else {
+        const float4 fa = *reinterpret_cast<const float4 *>(oa + off), fb = *reinterpret_cast<const float4 *>(ob + off);
+        xa[0] = fa.x; xa[1] = fa.y; xa[2] = fa.z; xa[3] = fa.w;
+        xb[0] = fb.x; xb[1] = fb.y; xb[2] = fb.z; xb[3] = fb.w;
+        float r[4];
+        for (int e = 0; e < 4; ++e) r[e] = (wa > 0.f ? wa * xa[e] : 0.f) + (wb > 0.f ? wb * xb[e] : 0.f);
+        *reinterpret_cast<float4 *>(o + off) = make_float4(r[0], r[1], r[2], r[3]);
+    }
+    if (lse != nullptr && c == 0) lse[row] = (sum > 0.f) ? M + logf(sum) : kNegInf;
+}
+
+hipError_t launch_lse_merge(const void *oa, const float *la, const void *ob, const float *lb, void *o, float *lse,
+                            long rows, int d, bool bf16, hipStream_t stream) {
+    const long threads = rows * (d / 4);
+    const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+    if (bf16)
+        hipLaunchKernelGGL(lse_merge_kernel<uint16_t>, grid, block, 0, stream, (const uint16_t *)oa, la,
+                           (const uint16_t *)ob, lb, (uint16_t *)o, lse, rows, d);
+    else
+        hipLaunchKernelGGL(lse_merge_kernel<float>, grid, block, 0, stream, (const float *)oa, la, (const float *)ob,
+                           lb, (float *)o, lse, rows, d);
     return hipGetLastError();
 }
 

@@ -77,11 +77,13 @@ __host__ __device__ inline void workgroup_order(int bid, int total, int nqb, int
 // The FULL tiles of query rows [qa, qz] (qz < n) are one contiguous run
 // [*t_lo, *t_hi) of the visiting order of band r (sink blocks, which hold a
 // position < g, are never FULL); an empty run is reported as [count, count).
-// Closed form of the per-tile test tile_full.
+// Closed form of the per-tile test tile_full.  klo > 0 restricts the keys
+// to positions >= klo (tiles reaching below it are not FULL).
 __host__ __device__ inline void full_range(const BandRange &r, int qa, int qz, int n, int w, int g, int bk,
-                                           int *t_lo, int *t_hi) {
+                                           int *t_lo, int *t_hi, int klo = 0) {
     int lo_key = qz - w + 1;  // smallest key every row of the block attends in the window
     if (lo_key < g) lo_key = g;
+    if (lo_key < klo) lo_key = klo;
     if (lo_key < 0) lo_key = 0;
     int kb_a = (lo_key + bk - 1) / bk;  // first block whose keys are all >= lo_key
     int kb_b = (qa + 1) / bk - 1;       // last block whose keys are all <= qa

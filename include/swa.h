@@ -146,6 +146,54 @@ int swa_decode_fwd_gqa(const void *q, const void *k_cache, const void *v_cache, 
 /* Workspace bytes of swa_decode_fwd_gqa (0 also for an invalid shape). */
 size_t swa_decode_workspace_bytes_gqa(int batch, int heads, int kv_heads, int d, int w, int g);
 
+/*
+ * Chunked prefill against the rolling cache: t new tokens of each batch entry
+ * b, at positions pos[b] .. pos[b]+t-1, attend the window and sinks of
+ * "Sliding Window and Sparse Attention, from Longformer to CSA2", s2 (the
+ * same set as swa_prefill_fwd would give those rows over the whole
+ * sequence).  Keys at positions >= pos[b] come from the chunk itself; keys
+ * at positions < pos[b] from the cache, which must hold positions
+ * 0 .. pos[b]-1 as written by swa_kv_append (ring row g + s mod w while the
+ * ring still holds s, else sink row s; "Local and Sparse Attention: Reading
+ * Fewer Token Positions", Figure 4 and the multi-token buffers it mentions).
+ * Call it before appending the chunk: the append overwrites ring rows that
+ * the chunk's first queries read.
+ *   q, o        : [batch][heads][t][d]   (dtype)
+ *   k_new, v_new: [batch][kv_heads][t][d]
+ *   k_cache, v_cache: [batch][kv_heads][g + w][d]
+ *   pos         : [batch] int64, device; a negative entry (or one with
+ *                 pos + t beyond INT_MAX) yields NaN rows for that entry
+ *   lse         : [batch][heads][t] fp32 or NULL
+ *   keys        : SWA_KEYS_ALL, or a partial attention over the cache keys
+ *                 only (SWA_KEYS_CACHE) or the chunk keys only
+ *                 (SWA_KEYS_CHUNK); a row with no key in its part gets
+ *                 o = 0 and lse = -inf, ready for swa_lse_merge.
+ * Grouping as in the _gqa calls (kv_heads == heads: multi-head attention).
+ * Errors: SWA_EINVAL (null pointer, sizes, keys, scale), SWA_EUNSUPPORTED
+ * (d or dtype), SWA_EALIGN (16-byte tensors, 8-byte pos, 4-byte lse).
+ */
+enum { SWA_KEYS_ALL = 0, SWA_KEYS_CACHE = 1, SWA_KEYS_CHUNK = 2 };
+int swa_chunk_prefill_fwd(const void *q, const void *k_new, const void *v_new,
+                          const void *k_cache, const void *v_cache, const int64_t *pos,
+                          void *o, float *lse, int batch, int heads, int kv_heads, int t, int d,
+                          int w, int g, float scale, float sink_bias, int keys,
+                          swa_dtype_t dtype, hipStream_t stream);
+
+/*
+ * Log-sum-exp merge of two partial attentions of the same query rows over
+ * disjoint key sets (s10 glossary of the first page above, LSE: the
+ * normaliser that lets partial results over disjoint key sets combine
+ * exactly): with M = max(lse_a, lse_b),
+ *   o   = (e^(lse_a-M) o_a + e^(lse_b-M) o_b) / (e^(lse_a-M) + e^(lse_b-M)),
+ *   lse = M + ln(e^(lse_a-M) + e^(lse_b-M)).
+ * A part with lse = -inf weighs 0; two empty parts give o = 0, lse = -inf.
+ *   o_a, o_b, o : [rows][d] (dtype; o may alias o_a or o_b)
+ *   (lse must not alias lse_a or lse_b: rows are merged by many threads)
+ *   lse_a, lse_b: [rows] fp32 (required); lse: [rows] fp32 or NULL
+ */
+int swa_lse_merge(const void *o_a, const float *lse_a, const void *o_b, const float *lse_b,
+                  void *o, float *lse, long long rows, int d, swa_dtype_t dtype, hipStream_t stream);
+
 /* Static description of a status code. */
 const char *swa_strerror(int status);
 

@@ -180,6 +180,26 @@ def expand_kv_heads(heads: int, x: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(np.take(x, idx, axis=-3))
 
 
+def lse_merge(o_a, lse_a, o_b, lse_b):
+    """Merge two partial attentions of the same rows over disjoint key sets
+    ("Sliding Window and Sparse Attention, from Longformer to CSA2", s10
+    glossary, LSE): each part's output weighs e^lse of that part.  A part
+    with lse = -inf weighs 0; two such parts give o = 0, lse = -inf.
+    o_*: [..., d], lse_*: [...]; fp64 results."""
+    o_a, o_b = _f64(o_a), _f64(o_b)
+    lse_a, lse_b = _f64(lse_a), _f64(lse_b)
+    m = np.maximum(lse_a, lse_b)
+    empty = np.isneginf(m)
+    m_safe = np.where(empty, 0.0, m)
+    wa = np.where(np.isneginf(lse_a), 0.0, np.exp(lse_a - m_safe))
+    wb = np.where(np.isneginf(lse_b), 0.0, np.exp(lse_b - m_safe))
+    tot = wa + wb
+    inv = np.where(tot > 0, 1.0 / np.where(tot > 0, tot, 1.0), 0.0)
+    o = (wa * inv)[..., None] * o_a + (wb * inv)[..., None] * o_b
+    lse = np.where(tot > 0, m_safe + np.log(np.where(tot > 0, tot, 1.0)), -np.inf)
+    return o, lse
+
+
 _DEFAULT: Oracle | None = None
 
 

@@ -148,3 +148,39 @@ def test_decode_gqa_workspace_sizes():
     assert swa.decode_workspace_bytes(64, 32, 128, 4096, 4, kv_heads=5) == 0   # invalid grouping
     # one key/value head for 8 query heads at batch 1: one job, 16 splits
     assert swa.decode_workspace_bytes(1, 8, 128, 4096, 4, kv_heads=1) == 8 * 16 * (2 + 128) * 4
+
+
+def _chunk(**kw):
+    a = dict(q=P, kn=P, vn=P, kc=P, vc=P, pos=P, o=P, lse=None, batch=1, heads=2, kv_heads=2, t=16, d=128, w=8,
+             g=0, scale=0.125, bias=0.0, keys=0, dtype=1)
+    a.update(kw)
+    return swa.lib().swa_chunk_prefill_fwd(a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["pos"], a["o"], a["lse"],
+                                           a["batch"], a["heads"], a["kv_heads"], a["t"], a["d"], a["w"], a["g"],
+                                           a["scale"], a["bias"], a["keys"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), EINVAL), (dict(kc=None), EINVAL), (dict(pos=None), EINVAL), (dict(o=None), EINVAL),
+    (dict(t=0), EINVAL), (dict(batch=0), EINVAL), (dict(w=0), EINVAL), (dict(g=-1), EINVAL),
+    (dict(keys=3), EINVAL), (dict(keys=-1), EINVAL), (dict(kv_heads=3), EINVAL), (dict(kv_heads=0), EINVAL),
+    (dict(scale=0.0), EINVAL), (dict(bias=float("inf")), EINVAL), (dict(t=1 << 24), EINVAL),
+    (dict(d=80), EUNSUP), (dict(dtype=5), EUNSUP),
+    (dict(kc=P + 8), EALIGN), (dict(vn=P + 4), EALIGN), (dict(pos=P + 4), EALIGN), (dict(lse=P + 2), EALIGN),
+])
+def test_chunk_prefill_rejects(kw, want):
+    assert _chunk(**kw) == want
+
+
+def _merge(**kw):
+    a = dict(oa=P, la=P, ob=P, lb=P, o=P, lse=None, rows=4, d=128, dtype=1)
+    a.update(kw)
+    return swa.lib().swa_lse_merge(a["oa"], a["la"], a["ob"], a["lb"], a["o"], a["lse"], a["rows"], a["d"],
+                                   a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(oa=None), EINVAL), (dict(lb=None), EINVAL), (dict(o=None), EINVAL), (dict(rows=0), EINVAL),
+    (dict(d=96), EUNSUP), (dict(dtype=9), EUNSUP), (dict(la=P + 2), EALIGN), (dict(ob=P + 8), EALIGN),
+])
+def test_lse_merge_rejects(kw, want):
+    assert _merge(**kw) == want
