@@ -46,6 +46,8 @@ DECODE = {
     "rolling_decode": (64, 32, 32, 128, 4096, 4, 4096, 131072, 4),
     # grouped-query attention: 4 query heads per key/value head
     "gqa_decode": (64, 32, 8, 128, 4096, 4, 4096, 131072, 4),
+    # the rolling-cache decode over an FP8 (E4M3) cache with per-head scales
+    "fp8_decode": (64, 32, 32, 128, 4096, 4, 4096, 131072, 4),
 }
 
 CHUNK = {
@@ -245,15 +247,23 @@ def bench_decode(name, steps, warmup):
 
     B, H, Hkv, d, w, g, lo, hi, seed = DECODE[name]
     dev = torch.device("cuda")
-    q, kc, vc, pos = synth.decode_problem(B, H, d, g + w, lo, hi, torch.bfloat16, seed=seed, device=dev,
-                                          kv_heads=Hkv)
+    fp8 = name.startswith("fp8")
+    if fp8:
+        q, kc, vc, ks, vs, pos = synth.fp8_decode_problem(B, H, Hkv, d, g + w, lo, hi, torch.bfloat16, seed=seed,
+                                                          device=dev)
+    else:
+        q, kc, vc, pos = synth.decode_problem(B, H, d, g + w, lo, hi, torch.bfloat16, seed=seed, device=dev,
+                                              kv_heads=Hkv)
     o = torch.empty_like(q)
     ws_bytes = swa.decode_workspace_bytes(B, H, d, w, g, kv_heads=Hkv)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step():
-        swa.decode(q, kc, vc, pos, w=w, g=g, out=o, workspace=ws)
+        if fp8:
+            swa.decode_fp8(q, kc, vc, ks, vs, pos, w=w, g=g, out=o, workspace=ws)
+        else:
+            swa.decode(q, kc, vc, pos, w=w, g=g, out=o, workspace=ws)
 
     for _ in range(warmup):
         step()
@@ -262,7 +272,7 @@ def bench_decode(name, steps, warmup):
     # algorithmic bytes: each (batch, key/value head)'s attended K and V rows
     # once (shared by the query heads of its group), plus q and o
     rows = sum(row_pairs(int(p), w, g) for p in pos.cpu().tolist()) * Hkv
-    nbytes = rows * d * 2 * 2 + 2 * B * H * d * 2
+    nbytes = rows * d * (1 if fp8 else 2) * 2 + 2 * B * H * d * 2
     achieved = nbytes / (ms_launch * 1e-3) / 1e9
     traffic = measured_traffic(name, "decode.hip")
     return {
@@ -273,7 +283,8 @@ def bench_decode(name, steps, warmup):
         "config": {"workload": name, "batch": B, "heads": H, "kv_heads": Hkv, "d": d, "w": w, "g": g,
                    "positions": [lo, hi], "kv_bytes_per_step": nbytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic, "kernel": "decode_kernel<bf16,128>",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": "decode_kernel<bf16,fp8,128>" if fp8 else "decode_kernel<bf16,bf16,128>",
                      "avg_launch_ms": ms_launch, "min_launch_ms": min(per)},
     }
 
@@ -344,7 +355,8 @@ def cpu_baseline_decode(name, budget_s=10.0):
         kpos = np.stack([np.concatenate([np.arange(p - w + 1, p + 1), np.arange(0, min(g, p - w + 1))])
                          for p in ps])
         orc.decode(q, ps, kpos, kk, vv, w=w, g=g)
-        done_bytes += sum(row_pairs(int(p), w, g) for p in ps) * d * 2 * 2 + 2 * units * d * 2
+        eb = 1 if name.startswith("fp8") else 2  # cache bytes per element
+        done_bytes += sum(row_pairs(int(p), w, g) for p in ps) * d * eb * 2 + 2 * units * d * 2
         done += units
     dt = time.perf_counter() - t0
     return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": orc.num_threads(), "kind": "oracle",

@@ -5,6 +5,7 @@ behind the C ABI of include/swa.h); this package is its thin Python binding.
 
     from block_sparse_causal_band_amd import prefill, kv_append, decode
     from block_sparse_causal_band_amd import chunk_prefill, lse_merge
+    from block_sparse_causal_band_amd import kv_append_fp8, decode_fp8
 
 Importing the package does not load the library; the first call does, and
 raises if it is not built (``python -m block_sparse_causal_band_amd.build``).
@@ -16,8 +17,10 @@ from .binding import (  # noqa: F401
     band_tiles,
     chunk_prefill,
     decode,
+    decode_fp8,
     decode_workspace_bytes,
     kv_append,
+    kv_append_fp8,
     lib,
     lse_merge,
     prefill,

@@ -64,6 +64,11 @@ def lib() -> ctypes.CDLL:
         L.swa_decode_workspace_bytes_gqa.restype = ctypes.c_size_t
         L.swa_chunk_prefill_fwd.argtypes = [_vp] * 8 + [_int] * 7 + [ctypes.c_float] * 2 + [_int, _int, _vp]
         L.swa_chunk_prefill_fwd.restype = _int
+        L.swa_kv_append_fp8.argtypes = [_vp] * 7 + [_int] * 6 + [_int, _vp]
+        L.swa_kv_append_fp8.restype = _int
+        L.swa_decode_fwd_fp8.argtypes = ([_vp] * 8 + [_int] * 6 + [ctypes.c_float] * 2 + [_int, _vp, ctypes.c_size_t,
+                                                                                           _vp])
+        L.swa_decode_fwd_fp8.restype = _int
         L.swa_lse_merge.argtypes = [_vp] * 6 + [ctypes.c_longlong, _int, _int, _vp]
         L.swa_lse_merge.restype = _int
         L.swa_strerror.argtypes = [_int]
@@ -161,6 +166,71 @@ def kv_append(k_cache, v_cache, k_new, v_new, pos, w: int, g: int = 0):
                              _dtype_code(k_cache), _stream(k_cache))
     if rc != 0:
         raise SwaError(rc, "swa_kv_append")
+
+
+def _fp8_scales(k_scale, v_scale, B, H):
+    import torch
+
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        _dev_tensor(t, name)
+        _need(t.dtype == torch.float32 and t.shape == (B, H), f"{name} must be fp32 [batch, kv_heads]")
+
+
+def kv_append_fp8(k_cache, v_cache, k_new, v_new, pos, k_scale, v_scale, w: int, g: int = 0):
+    """Quantise k_new, v_new [batch, heads, t, d] (bf16 or fp32) to E4M3 codes
+    (uint8 caches [batch, heads, g + w, d]) with per-(batch, head) fp32 scales
+    [batch, heads], at positions pos[b] .. pos[b]+t-1."""
+    import torch
+
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("k_new", k_new), ("v_new", v_new), ("pos", pos)):
+        _dev_tensor(t, name)
+    _need(k_cache.dtype == v_cache.dtype == torch.uint8, "fp8 caches are uint8 tensors of E4M3 codes")
+    B, H, R, d = k_cache.shape
+    _need(v_cache.shape == k_cache.shape, "k_cache and v_cache must share one shape")
+    _need(R == g + w, f"cache must hold g + w = {g + w} rows per (batch, head)")
+    _need(k_new.dim() == 4 and k_new.shape[:2] == (B, H) and k_new.shape[3] == d, "k_new must be [batch, heads, t, d]")
+    _need(v_new.shape == k_new.shape and v_new.dtype == k_new.dtype, "v_new must match k_new")
+    _need(pos.dtype == torch.int64 and pos.shape == (B,), "pos must be int64 [batch]")
+    _fp8_scales(k_scale, v_scale, B, H)
+    rc = lib().swa_kv_append_fp8(k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                 pos.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(), B, H, k_new.shape[2], d,
+                                 int(w), int(g), _dtype_code(k_new), _stream(k_cache))
+    if rc != 0:
+        raise SwaError(rc, "swa_kv_append_fp8")
+
+
+def decode_fp8(q, k_cache, v_cache, k_scale, v_scale, pos, w: int, g: int = 0, scale: float | None = None,
+               sink_bias: float = 0.0, return_lse: bool = False, workspace=None, out=None):
+    """decode() over E4M3 caches (uint8 [batch, kv_heads, g + w, d]) with fp32
+    scales [batch, kv_heads]; q and the output bf16 or fp32."""
+    import torch
+
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("pos", pos)):
+        _dev_tensor(t, name)
+    B, H, d = q.shape
+    _need(k_cache.dim() == 4 and k_cache.dtype == v_cache.dtype == torch.uint8, "fp8 caches are uint8 [b, hkv, r, d]")
+    Hkv = k_cache.shape[1]
+    _need(k_cache.shape == v_cache.shape == (B, Hkv, g + w, d), "caches must be [batch, kv_heads, g + w, d]")
+    _need(pos.dtype == torch.int64 and pos.shape == (B,), "pos must be int64 [batch]")
+    _fp8_scales(k_scale, v_scale, B, Hkv)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    _dev_tensor(o, "out")
+    _need(o.shape == q.shape and o.dtype == q.dtype, "out must match q")
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if return_lse else None
+    need = decode_workspace_bytes(B, H, d, w, g, kv_heads=Hkv)
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().swa_decode_fwd_fp8(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), k_scale.data_ptr(),
+                                  v_scale.data_ptr(), pos.data_ptr(), o.data_ptr(),
+                                  lse.data_ptr() if lse is not None else None, B, H, Hkv, d, int(w), int(g),
+                                  float(scale), float(sink_bias), _dtype_code(q), ws_ptr, ws_bytes, _stream(q))
+    if rc != 0:
+        raise SwaError(rc, "swa_decode_fwd_fp8")
+    return (o, lse) if return_lse else o
 
 
 def decode_workspace_bytes(batch: int, heads: int, d: int, w: int, g: int, kv_heads: int | None = None) -> int:

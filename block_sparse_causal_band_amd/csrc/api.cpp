@@ -18,11 +18,17 @@ hipError_t launch_decode(const void *q, const void *kc, const void *vc, const in
                          bool bf16, void *ws, hipStream_t stream);
 hipError_t launch_kv_append(void *kc, void *vc, const void *kn, const void *vn, const int64_t *pos, int batch,
                             int heads, int tn, int d, int w, int g, bool bf16, hipStream_t stream);
-size_t decode_workspace_bytes(int batch, int heads, int kv_heads, int d, int rows);
+size_t decode_workspace_bytes(int batch, int heads, int kv_heads, int d, int rows, int cap = 8);
 hipError_t launch_chunk_prefill(const void *q, const void *k_new, const void *v_new, const void *k_cache,
                                 const void *v_cache, const int64_t *pos, void *o, float *lse, int batch, int heads,
                                 int kv_heads, int t, int d, int w, int g, float scale, float sink_bias, int part,
                                 bool bf16, hipStream_t stream);
+hipError_t launch_kv_append_fp8(void *kc, void *vc, const void *kn, const void *vn, const int64_t *pos,
+                                const float *ksc, const float *vsc, int batch, int heads, int tn, int d, int w,
+                                int g, bool bf16, hipStream_t stream);
+hipError_t launch_decode_fp8(const void *q, const void *kc, const void *vc, const float *ksc, const float *vsc,
+                             const int64_t *pos, void *o, float *lse, int batch, int heads, int kv_heads, int d,
+                             int w, int g, float scale, float sink_bias, bool bf16, void *ws, hipStream_t stream);
 hipError_t launch_lse_merge(const void *oa, const float *la, const void *ob, const float *lb, void *o, float *lse,
                             long rows, int d, bool bf16, hipStream_t stream);
 int prefill_rows_per_workgroup(bool bf16);
@@ -141,6 +147,50 @@ int swa_lse_merge(const void *o_a, const float *lse_a, const void *o_b, const fl
         (lse && !aligned4(lse)))
         return SWA_EALIGN;
     return status_of(swa::launch_lse_merge(o_a, lse_a, o_b, lse_b, o, lse, (long)rows, d, dtype == SWA_BF16, stream));
+}
+
+int swa_kv_append_fp8(void *k_cache, void *v_cache, const void *k_new, const void *v_new, const int64_t *pos,
+                      const float *k_scale, const float *v_scale, int batch, int heads, int t_new, int d, int w,
+                      int g, swa_dtype_t dtype, hipStream_t stream) {
+    if (!k_cache || !v_cache || !k_new || !v_new || !pos || !k_scale || !v_scale) return SWA_EINVAL;
+    if (batch < 1 || heads < 1 || t_new < 0 || w < 1 || g < 0) return SWA_EINVAL;
+    if ((long long)g + w > INT_MAX) return SWA_EINVAL;
+    int st = check_dtype_d(dtype, d);
+    if (st != SWA_OK) return st;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new) ||
+        (reinterpret_cast<uintptr_t>(pos) & 7u) || !aligned4(k_scale) || !aligned4(v_scale))
+        return SWA_EALIGN;
+    if (t_new == 0) return SWA_OK;
+    const long long blocks = ((long long)batch * heads * t_new * (d / 8) + 255) / 256;
+    if (blocks > INT_MAX) return SWA_EINVAL;
+    return status_of(swa::launch_kv_append_fp8(k_cache, v_cache, k_new, v_new, pos, k_scale, v_scale, batch, heads,
+                                               t_new, d, w, g, dtype == SWA_BF16, stream));
+}
+
+int swa_decode_fwd_fp8(const void *q, const void *k_cache, const void *v_cache, const float *k_scale,
+                       const float *v_scale, const int64_t *pos, void *o, float *lse, int batch, int heads,
+                       int kv_heads, int d, int w, int g, float scale, float sink_bias, swa_dtype_t dtype,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !pos || !o) return SWA_EINVAL;
+    if (batch < 1 || heads < 1 || w < 1 || g < 0) return SWA_EINVAL;
+    if (kv_heads < 1 || kv_heads > heads || heads % kv_heads != 0) return SWA_EINVAL;
+    if ((long long)g + w > INT_MAX / 2) return SWA_EINVAL;
+    if ((long long)batch * heads > INT_MAX / 64) return SWA_EINVAL;
+    if (!std::isfinite(scale) || !(scale > 0.f) || !std::isfinite(sink_bias)) return SWA_EINVAL;
+    int st = check_dtype_d(dtype, d);
+    if (st != SWA_OK) return st;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+        (reinterpret_cast<uintptr_t>(pos) & 7u) || (lse && !aligned4(lse)) || !aligned4(k_scale) ||
+        !aligned4(v_scale))
+        return SWA_EALIGN;
+    const size_t need = swa::decode_workspace_bytes(batch, heads, kv_heads, d, g + w, 4);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return SWA_EWORKSPACE;
+        if (!aligned16(workspace)) return SWA_EALIGN;
+    }
+    return status_of(swa::launch_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, pos, o, lse, batch, heads,
+                                            kv_heads, d, w, g, scale, sink_bias, dtype == SWA_BF16, workspace,
+                                            stream));
 }
 
 size_t swa_decode_workspace_bytes_gqa(int batch, int heads, int kv_heads, int d, int w, int g) {

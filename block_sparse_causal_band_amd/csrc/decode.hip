@@ -33,32 +33,67 @@
 namespace swa {
 
 constexpr int kDecThreads = 256;
-constexpr int kDecUnroll = 4;  // row loads in flight per lane per step, for K and for V each
 
-template <bool BF16, int D>
-struct DecodeCfg {
-    using T = typename std::conditional<BF16, uint16_t, float>::type;
-    static constexpr int kEPC = BF16 ? 8 : 4;     // elements per 16-byte chunk
-    static constexpr int kLPR = D / kEPC;         // lanes per cache row
-    static constexpr int kRPI = 64 / kLPR;        // rows per wave-wide load
-    static constexpr int kGroups = (kDecThreads / 64) * kRPI;  // row groups per workgroup
-    static constexpr int kRowsPerStep = (kDecThreads / 64) * kDecUnroll * kRPI;
+// Cache element kinds: each lane reads one chunk of kEPC elements (kBytes)
+// of a row per load; kUnroll rows per lane are in flight, for K and for V.
+struct CacheBf16 {
+    static constexpr int kEPC = 8, kBytes = 16, kUnroll = 4;
+};
+struct CacheF32 {
+    static constexpr int kEPC = 4, kBytes = 16, kUnroll = 4;
+};
+struct CacheFp8 {  // OCP E4M3 bytes, 8 per lane: the same lane layout as bf16, twice the rows in flight
+    static constexpr int kEPC = 8, kBytes = 8, kUnroll = 8;
 };
 
-template <bool BF16>
-__device__ __forceinline__ void unpack(const uint4 &x, float *f) {
-    if constexpr (BF16) {
+template <typename CK, int D>
+struct DecodeCfg {
+    using V = typename std::conditional<CK::kBytes == 16, uint4, uint2>::type;  // one lane's chunk
+    static constexpr int kEPC = CK::kEPC;
+    static constexpr int kLPR = D / kEPC;         // lanes per cache row
+    static constexpr int kRPI = 64 / kLPR;        // rows per wave-wide load
+    static constexpr int kUnroll = CK::kUnroll;
+    static constexpr int kRowBytes = D * CK::kBytes / CK::kEPC;
+    static constexpr int kGroups = (kDecThreads / 64) * kRPI;  // row groups per workgroup
+    static constexpr int kRowsPerStep = (kDecThreads / 64) * kUnroll * kRPI;
+};
+
+__device__ __forceinline__ void load_chunk(const uint8_t *p, uint4 &x) { x = load_stream16(p); }
+__device__ __forceinline__ void load_chunk(const uint8_t *p, uint2 &x) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+    x = make_uint2(v[0], v[1]);
+}
+__device__ __forceinline__ void zero_chunk(uint4 &x) { x = make_uint4(0, 0, 0, 0); }
+__device__ __forceinline__ void zero_chunk(uint2 &x) { x = make_uint2(0, 0); }
+
+// chunk -> fp32 values (fp8: the hardware conversion of OCP E4M3, exact)
+template <typename CK>
+__device__ __forceinline__ void unpack(const typename DecodeCfg<CK, 64>::V &x, float *f) {
+    if constexpr (std::is_same<CK, CacheBf16>::value) {
         const uint32_t *u = reinterpret_cast<const uint32_t *>(&x);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             f[2 * i] = bf16lo(u[i]);
             f[2 * i + 1] = bf16hi(u[i]);
         }
-    } else {
+    } else if constexpr (std::is_same<CK, CacheF32>::value) {
         f[0] = __uint_as_float(x.x);
         f[1] = __uint_as_float(x.y);
         f[2] = __uint_as_float(x.z);
         f[3] = __uint_as_float(x.w);
+    } else {
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        const uint32_t u[2] = {x.x, x.y};
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)u[i], false);
+            const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)u[i], true);
+            f[4 * i + 0] = a.x;
+            f[4 * i + 1] = a.y;
+            f[4 * i + 2] = b.x;
+            f[4 * i + 3] = b.y;
+        }
     }
 }
 
@@ -88,15 +123,20 @@ __device__ __forceinline__ float group_sum(float x) {
 // Partial state of one workgroup: m (raw q.k units incl. bias), l, o[D]
 // (unnormalised), for each of its GQ query heads.  The GQ query heads share
 // one key/value head (grouped-query attention), so each cache row is read
-// once for all of them.
-template <bool BF16, int D, int GQ>
+// once for all of them.  QT: type of q and o (bf16 bits or fp32); CK: cache
+// element kind.  An fp8 cache carries one scale per (batch, key/value head)
+// for K (ksc) and V (vsc): a row's value is scale x its E4M3 value.
+template <typename QT, typename CK, int D, int GQ>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const void *__restrict__ qp, const void *__restrict__ kcp, const void *__restrict__ vcp,
     const int64_t *__restrict__ pos, void *__restrict__ op, float *__restrict__ lsep, int heads, int kv_heads,
-    int w, int g, float c2, float scale, float bias_raw, int splits, int rows_per_split, float *__restrict__ ws) {
-    using C = DecodeCfg<BF16, D>;
-    using T = typename C::T;
-    constexpr int EPC = C::kEPC, LPR = C::kLPR, RPI = C::kRPI;
+    int w, int g, float c2, float scale, float bias_raw, int splits, int rows_per_split, float *__restrict__ ws,
+    const float *__restrict__ ksc, const float *__restrict__ vsc) {
+    using C = DecodeCfg<CK, D>;
+    using CV = typename C::V;
+    constexpr int EPC = C::kEPC, LPR = C::kLPR, RPI = C::kRPI, UN = C::kUnroll;
+    constexpr bool kDot2 = std::is_same<QT, uint16_t>::value && std::is_same<CK, CacheBf16>::value;
+    constexpr bool kFp8 = std::is_same<CK, CacheFp8>::value;
     __shared__ float sh_m[C::kGroups], sh_l[C::kGroups];
     __shared__ float sh_o[C::kGroups][D];
 
@@ -113,19 +153,32 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const int unit0 = b * heads + h0;          // batch * heads + query head of head 0
     const int R = g + w;
     const int64_t p = pos[b];
+    const float kscale = kFp8 ? ksc[kvu] : 1.f;
+    const float vscale = kFp8 ? vsc[kvu] : 1.f;
 
-    const T *kc = reinterpret_cast<const T *>(kcp) + (size_t)kvu * R * D;
-    const T *vc = reinterpret_cast<const T *>(vcp) + (size_t)kvu * R * D;
+    const uint8_t *kc = reinterpret_cast<const uint8_t *>(kcp) + (size_t)kvu * R * C::kRowBytes;
+    const uint8_t *vc = reinterpret_cast<const uint8_t *>(vcp) + (size_t)kvu * R * C::kRowBytes;
 
-    // the lane's chunk of each query: fp32 values, and for bf16 also the
-    // packed pairs that the q.k dot2 instructions take as they are
+    // the lane's EPC elements of each query: fp32 values, and for bf16 q over a
+    // bf16 cache also the packed pairs that the q.k dot2 instructions take
     float qf[GQ][EPC];
     uint4 qx[GQ];
 #pragma unroll
     for (int j = 0; j < GQ; ++j) {
-        const T *q = reinterpret_cast<const T *>(qp) + (size_t)(unit0 + j) * D;
-        qx[j] = *reinterpret_cast<const uint4 *>(q + sub * EPC);
-        if constexpr (!BF16) unpack<BF16>(qx[j], qf[j]);
+        const QT *q = reinterpret_cast<const QT *>(qp) + (size_t)(unit0 + j) * D + sub * EPC;
+        if constexpr (std::is_same<QT, uint16_t>::value) {
+            qx[j] = *reinterpret_cast<const uint4 *>(q);
+            if constexpr (!kDot2) unpack<CacheBf16>(qx[j], qf[j]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < EPC; e += 4) {
+                const float4 f = *reinterpret_cast<const float4 *>(q + e);
+                qf[j][e] = f.x;
+                qf[j][e + 1] = f.y;
+                qf[j][e + 2] = f.z;
+                qf[j][e + 3] = f.w;
+            }
+        }
     }
 
     // ring geometry for this query position
@@ -145,23 +198,23 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const int r_begin = split * rows_per_split;
     const int r_end = min(R, r_begin + rows_per_split);
     for (int r0 = r_begin; r0 < r_end; r0 += C::kRowsPerStep) {
-        uint4 kx[kDecUnroll], vx[kDecUnroll];
-        int rows[kDecUnroll];
+        CV kx[UN], vx[UN];
+        int rows[UN];
 #pragma unroll
-        for (int u = 0; u < kDecUnroll; ++u) {
-            int r = r0 + (wave * kDecUnroll + u) * RPI + grp_in_wave;
+        for (int u = 0; u < UN; ++u) {
+            int r = r0 + (wave * UN + u) * RPI + grp_in_wave;
             rows[u] = r;
             if (r < r_end) {
-                kx[u] = load_stream16(kc + (size_t)r * D + sub * EPC);
-                vx[u] = load_stream16(vc + (size_t)r * D + sub * EPC);
+                load_chunk(kc + (size_t)r * C::kRowBytes + sub * CK::kBytes, kx[u]);
+                load_chunk(vc + (size_t)r * C::kRowBytes + sub * CK::kBytes, vx[u]);
             } else {
-                kx[u] = make_uint4(0, 0, 0, 0);
-                vx[u] = make_uint4(0, 0, 0, 0);
+                zero_chunk(kx[u]);
+                zero_chunk(vx[u]);
             }
         }
-        float s[GQ][kDecUnroll];
+        float s[GQ][UN];
 #pragma unroll
-        for (int u = 0; u < kDecUnroll; ++u) {
+        for (int u = 0; u < UN; ++u) {
             // which position does row r hold, and is it read?
             int r = rows[u];
             bool valid;
@@ -185,33 +238,39 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                 }
             }
             const float bias = (t < g) ? bias_raw : 0.f;
+            // a row that is not read may hold anything (an unwritten slot):
+            // its score is -inf and its value chunk is zeroed, so that 0 * NaN
+            // cannot reach the output
+            if (!valid) zero_chunk(vx[u]);
+            float kf[EPC];
+            if constexpr (!kDot2) unpack<CK>(kx[u], kf);
 #pragma unroll
             for (int j = 0; j < GQ; ++j) {
                 float acc = 0.f;
-                if constexpr (BF16) {
+                if constexpr (kDot2) {
                     // bf16 pairs straight from the cache: products exact, fp32 sums
                     const bf16x2 *k2 = reinterpret_cast<const bf16x2 *>(&kx[u]);
                     const bf16x2 *q2 = reinterpret_cast<const bf16x2 *>(&qx[j]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_fdot2_f32_bf16(q2[e], k2[e], acc, false);
                 } else {
-                    float kf[EPC];
-                    unpack<BF16>(kx[u], kf);
 #pragma unroll
                     for (int e = 0; e < EPC; ++e) acc = fmaf(qf[j][e], kf[e], acc);
                 }
-                acc = group_sum<LPR>(acc) + bias;
+                acc = group_sum<LPR>(acc);
+                if constexpr (kFp8) acc *= kscale;
+                acc += bias;
                 s[j][u] = valid ? acc : kNegInf;
             }
         }
-        float vf[kDecUnroll][EPC];
+        float vf[UN][EPC];
 #pragma unroll
-        for (int u = 0; u < kDecUnroll; ++u) unpack<BF16>(vx[u], vf[u]);
+        for (int u = 0; u < UN; ++u) unpack<CK>(vx[u], vf[u]);
 #pragma unroll
         for (int j = 0; j < GQ; ++j) {
             float mx = s[j][0];
 #pragma unroll
-            for (int u = 1; u < kDecUnroll; ++u) mx = fmaxf(mx, s[j][u]);
+            for (int u = 1; u < UN; ++u) mx = fmaxf(mx, s[j][u]);
             const float m_new = fmaxf(m[j], mx);
             const float m_use = (m_new == kNegInf) ? 0.f : m_new;
             const float alpha = fast_exp2((m[j] - m_use) * c2);
@@ -220,7 +279,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
 #pragma unroll
             for (int e = 0; e < EPC; ++e) o[j][e] *= alpha;
 #pragma unroll
-            for (int u = 0; u < kDecUnroll; ++u) {
+            for (int u = 0; u < UN; ++u) {
                 const float pu = fast_exp2(fmaf(s[j][u], c2, neg));
                 l[j] += pu;
 #pragma unroll
@@ -251,14 +310,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         for (int gi = 0; gi < C::kGroups; ++gi) L += sh_l[gi] * fast_exp2((sh_m[gi] - M_use) * c2);
 
         if (splits == 1) {
-            const float inv = (L > 0.f) ? 1.f / L : __builtin_nanf("");
-            T *out = reinterpret_cast<T *>(op) + (size_t)unit * D;
+            const float inv = (L > 0.f) ? vscale / L : __builtin_nanf("");
+            QT *out = reinterpret_cast<QT *>(op) + (size_t)unit * D;
             for (int c = tid; c < D; c += kDecThreads) {
                 float acc = 0.f;
 #pragma unroll
                 for (int gi = 0; gi < C::kGroups; ++gi) acc += sh_o[gi][c] * fast_exp2((sh_m[gi] - M_use) * c2);
                 float x = acc * inv;
-                if constexpr (BF16)
+                if constexpr (std::is_same<QT, uint16_t>::value)
                     out[c] = (uint16_t)f32_to_bf16_bits(x);
                 else
                     out[c] = x;
@@ -270,7 +329,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                 float acc = 0.f;
 #pragma unroll
                 for (int gi = 0; gi < C::kGroups; ++gi) acc += sh_o[gi][c] * fast_exp2((sh_m[gi] - M_use) * c2);
-                rec[2 + c] = acc;
+                rec[2 + c] = acc * vscale;
             }
             if (tid == 0) {
                 rec[0] = M;
@@ -281,11 +340,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
 }
 
 // Merge S partial states of one (batch, head) by log-sum-exp.
-template <bool BF16, int D>
+template <typename QT, int D>
 __global__ __launch_bounds__(D) void decode_merge_kernel(const float *__restrict__ ws, void *__restrict__ op,
                                                          float *__restrict__ lsep, int splits, float c2,
                                                          float scale) {
-    using T = typename std::conditional<BF16, uint16_t, float>::type;
     const int unit = blockIdx.x, c = threadIdx.x;
     const float *rec = ws + (size_t)unit * splits * (2 + D);
     float M = kNegInf;
@@ -299,21 +357,25 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float *__restrict
         acc += r[2 + c] * f;
     }
     float x = (L > 0.f) ? acc / L : __builtin_nanf("");
-    T *out = reinterpret_cast<T *>(op) + (size_t)unit * D;
-    if constexpr (BF16)
+    QT *out = reinterpret_cast<QT *>(op) + (size_t)unit * D;
+    if constexpr (std::is_same<QT, uint16_t>::value)
         out[c] = (uint16_t)f32_to_bf16_bits(x);
     else
         out[c] = x;
     if (lsep != nullptr && c == 0) lsep[unit] = (L > 0.f) ? M * scale + logf(L) : __builtin_nanf("");
 }
 
-// Query heads per decode workgroup: the largest power of two <= 8 that
-// divides the group size (query heads per key/value head).
-int decode_heads_per_wg(int group) {
+// Query heads per decode workgroup: the largest power of two <= cap that
+// divides the group size (query heads per key/value head).  fp8 caches cap
+// it at 4 (twice the rows in flight per lane leave registers for 4 heads).
+int decode_heads_per_wg(int group, int cap) {
     int gq = 1;
-    while (gq < 8 && group % (2 * gq) == 0) gq *= 2;
+    while (gq < cap && group % (2 * gq) == 0) gq *= 2;
     return gq;
 }
+
+template <typename CK>
+constexpr int heads_cap() { return std::is_same<CK, CacheFp8>::value ? 4 : 8; }
 
 // Split count: enough workgroups to cover the chip, at least 256 cache rows each.
 int decode_splits(int jobs, int rows) {
@@ -327,56 +389,91 @@ int decode_splits(int jobs, int rows) {
 }
 
 // jobs = batch * heads / (query heads per workgroup): workgroups before splitting
-static int decode_jobs(int batch, int heads, int kv_heads) {
-    return batch * (heads / decode_heads_per_wg(heads / kv_heads));
+static int decode_jobs(int batch, int heads, int kv_heads, int cap) {
+    return batch * (heads / decode_heads_per_wg(heads / kv_heads, cap));
 }
 
-size_t decode_workspace_bytes(int batch, int heads, int kv_heads, int d, int rows) {
-    int s = decode_splits(decode_jobs(batch, heads, kv_heads), rows);
+// Workspace of a launch (0 when it does not split); an fp8 launch (cap 4)
+// never needs more than a bf16/fp32 one (cap 8) of the same shape.
+size_t decode_workspace_bytes(int batch, int heads, int kv_heads, int d, int rows, int cap) {
+    int s = decode_splits(decode_jobs(batch, heads, kv_heads, cap), rows);
     if (s == 1) return 0;
     return (size_t)batch * heads * s * (2 + d) * sizeof(float);
 }
 
-template <bool BF16, int D, int GQ>
+template <typename QT, typename CK, int D, int GQ>
 static hipError_t launch_decode_t(const void *q, const void *kc, const void *vc, const int64_t *pos, void *o,
                                   float *lse, int batch, int heads, int kv_heads, int w, int g, float scale,
-                                  float sink_bias, void *ws, hipStream_t stream) {
+                                  float sink_bias, void *ws, const float *ksc, const float *vsc,
+                                  hipStream_t stream) {
     const int R = g + w;
-    const int jobs = decode_jobs(batch, heads, kv_heads);
+    const int jobs = decode_jobs(batch, heads, kv_heads, heads_cap<CK>());
     const int splits = decode_splits(jobs, R);
     const int rps = (R + splits - 1) / splits;
     const float c2 = (float)((double)scale * kLog2e);
     const float bias_raw = (float)((double)sink_bias / (double)scale);
-    hipLaunchKernelGGL((decode_kernel<BF16, D, GQ>), dim3(jobs * splits), dim3(kDecThreads), 0, stream, q, kc, vc,
-                       pos, o, lse, heads, kv_heads, w, g, c2, scale, bias_raw, splits, rps, (float *)ws);
+    hipLaunchKernelGGL((decode_kernel<QT, CK, D, GQ>), dim3(jobs * splits), dim3(kDecThreads), 0, stream, q, kc,
+                       vc, pos, o, lse, heads, kv_heads, w, g, c2, scale, bias_raw, splits, rps, (float *)ws, ksc,
+                       vsc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
-    hipLaunchKernelGGL((decode_merge_kernel<BF16, D>), dim3(batch * heads), dim3(D), 0, stream, (const float *)ws,
-                       o, lse, splits, c2, scale);
+    hipLaunchKernelGGL((decode_merge_kernel<QT, D>), dim3(batch * heads), dim3(D), 0, stream, (const float *)ws, o,
+                       lse, splits, c2, scale);
     return hipGetLastError();
 }
 
-template <bool BF16, int D>
+template <typename QT, typename CK, int D>
 static hipError_t launch_decode_d(const void *q, const void *kc, const void *vc, const int64_t *pos, void *o,
                                   float *lse, int batch, int heads, int kv_heads, int w, int g, float scale,
-                                  float sink_bias, void *ws, hipStream_t stream) {
-    switch (decode_heads_per_wg(heads / kv_heads)) {
-        case 8: return launch_decode_t<BF16, D, 8>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale, sink_bias, ws, stream);
-        case 4: return launch_decode_t<BF16, D, 4>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale, sink_bias, ws, stream);
-        case 2: return launch_decode_t<BF16, D, 2>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale, sink_bias, ws, stream);
-        default: return launch_decode_t<BF16, D, 1>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale, sink_bias, ws, stream);
+                                  float sink_bias, void *ws, const float *ksc, const float *vsc,
+                                  hipStream_t stream) {
+#define SWA_DEC(GQ)                                                                                              \
+    launch_decode_t<QT, CK, D, GQ>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale, sink_bias, ws, \
+                                   ksc, vsc, stream)
+    switch (decode_heads_per_wg(heads / kv_heads, heads_cap<CK>())) {
+        case 8:
+            if constexpr (heads_cap<CK>() >= 8) return SWA_DEC(8);
+            return hipErrorInvalidValue;
+        case 4: return SWA_DEC(4);
+        case 2: return SWA_DEC(2);
+        default: return SWA_DEC(1);
     }
+#undef SWA_DEC
 }
 
 hipError_t launch_decode(const void *q, const void *kc, const void *vc, const int64_t *pos, void *o, float *lse,
                          int batch, int heads, int kv_heads, int d, int w, int g, float scale, float sink_bias,
                          bool bf16, void *ws, hipStream_t stream) {
     if (bf16) {
-        if (d == 128) return launch_decode_d<true, 128>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale, sink_bias, ws, stream);
-        return launch_decode_d<true, 64>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale, sink_bias, ws, stream);
+        if (d == 128)
+            return launch_decode_d<uint16_t, CacheBf16, 128>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g,
+                                                             scale, sink_bias, ws, nullptr, nullptr, stream);
+        return launch_decode_d<uint16_t, CacheBf16, 64>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale,
+                                                        sink_bias, ws, nullptr, nullptr, stream);
     }
-    if (d == 128) return launch_decode_d<false, 128>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale, sink_bias, ws, stream);
-    return launch_decode_d<false, 64>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale, sink_bias, ws, stream);
+    if (d == 128)
+        return launch_decode_d<float, CacheF32, 128>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale,
+                                                     sink_bias, ws, nullptr, nullptr, stream);
+    return launch_decode_d<float, CacheF32, 64>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale,
+                                                sink_bias, ws, nullptr, nullptr, stream);
+}
+
+// fp8 (E4M3) caches with per-(batch, key/value head) scales; q and o bf16 or fp32.
+hipError_t launch_decode_fp8(const void *q, const void *kc, const void *vc, const float *ksc, const float *vsc,
+                             const int64_t *pos, void *o, float *lse, int batch, int heads, int kv_heads, int d,
+                             int w, int g, float scale, float sink_bias, bool bf16, void *ws, hipStream_t stream) {
+    if (bf16) {
+        if (d == 128)
+            return launch_decode_d<uint16_t, CacheFp8, 128>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g,
+                                                            scale, sink_bias, ws, ksc, vsc, stream);
+        return launch_decode_d<uint16_t, CacheFp8, 64>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale,
+                                                       sink_bias, ws, ksc, vsc, stream);
+    }
+    if (d == 128)
+        return launch_decode_d<float, CacheFp8, 128>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale,
+                                                     sink_bias, ws, ksc, vsc, stream);
+    return launch_decode_d<float, CacheFp8, 64>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale,
+                                                sink_bias, ws, ksc, vsc, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -429,6 +526,107 @@ hipError_t launch_kv_append(void *kc, void *vc, const void *kn, const void *vn, 
     else
         hipLaunchKernelGGL(kv_append_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, stream, (uint8_t *)kc,
                            (uint8_t *)vc, (const uint8_t *)kn, (const uint8_t *)vn, pos, heads, tn, d, w, g, total);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// fp8 cache append.  E4M3 in its OCP form ("Sliding Window and Sparse
+// Attention, from Longformer to CSA2", s10 glossary, E4M3: 1 sign, 4
+// exponent, 3 mantissa bits; exponent bias 7, no infinities, S.1111.111 is
+// NaN, largest finite 448).  A value x of key/value head (b, h) is stored as
+// the code of y = x / scale[b][h] (fp32 division, correctly rounded), y
+// rounded to the nearest code with ties to even mantissa and |y| >= 448
+// saturated to 448; NaN stays NaN.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+    const uint32_t bits = __float_as_uint(y);
+    const uint32_t sign = (bits >> 24) & 0x80u;
+    const uint32_t a = bits & 0x7fffffffu;
+    if (a > 0x7f800000u) return sign | 0x7fu;  // NaN
+    if (a >= 0x43e00000u) return sign | 0x7eu;  // |y| >= 448 (and infinity): saturate
+    if (a < 0x3c800000u) {                      // |y| < 2^-6: multiples of 2^-9
+        const float m = __builtin_rintf(__uint_as_float(a) * 512.f);  // exact scaling, then ties to even
+        return sign | (uint32_t)m;              // m = 8 is the smallest normal's code
+    }
+    // keep 3 mantissa bits, ties to even (a carry moves into the exponent),
+    // then rebias the exponent from 127 to 7
+    const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
+    return sign | ((r >> 20) - (120u << 3));
+}
+
+// One thread quantises 8 consecutive elements of one K row and one V row
+// and writes them where kv_append_kernel would write the bf16/fp32 row.
+template <bool BF16>
+__global__ __launch_bounds__(256) void kv_append_fp8_kernel(uint8_t *__restrict__ kc, uint8_t *__restrict__ vc,
+                                                            const void *__restrict__ kn, const void *__restrict__ vn,
+                                                            const int64_t *__restrict__ pos,
+                                                            const float *__restrict__ ksc,
+                                                            const float *__restrict__ vsc, int heads, int tn, int d,
+                                                            int w, int g, long long total) {
+    const long long id = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (id >= total) return;
+    const int cpr = d / 8;  // 8-element pieces per row
+    const int piece = (int)(id % cpr);
+    const long long rowid = id / cpr;
+    const int j = (int)(rowid % tn);
+    const long long unit = rowid / tn;  // batch * heads + head
+    const int b = (int)(unit / heads);
+    const int64_t P0 = pos[b];
+    if (P0 < 0) return;
+    const int64_t P = P0 + j;
+    const size_t src = ((size_t)unit * tn + j) * d + (size_t)piece * 8;  // element index
+    float xk[8], xv[8];
+    if constexpr (BF16) {
+        const uint4 a = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(kn) + src);
+        const uint4 c = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(vn) + src);
+        const uint32_t ua[4] = {a.x, a.y, a.z, a.w}, uc[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            xk[2 * i] = bf16lo(ua[i]);
+            xk[2 * i + 1] = bf16hi(ua[i]);
+            xv[2 * i] = bf16lo(uc[i]);
+            xv[2 * i + 1] = bf16hi(uc[i]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; i += 4) {
+            const float4 a = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(kn) + src + i);
+            const float4 c = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(vn) + src + i);
+            xk[i] = a.x; xk[i + 1] = a.y; xk[i + 2] = a.z; xk[i + 3] = a.w;
+            xv[i] = c.x; xv[i + 1] = c.y; xv[i + 2] = c.z; xv[i + 3] = c.w;
+        }
+    }
+    const float sk = ksc[unit], sv = vsc[unit];
+    uint32_t k8[2] = {0, 0}, v8[2] = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        k8[i >> 2] |= e4m3_code(__fdiv_rn(xk[i], sk)) << (8 * (i & 3));
+        v8[i >> 2] |= e4m3_code(__fdiv_rn(xv[i], sv)) << (8 * (i & 3));
+    }
+    const uint2 kk = make_uint2(k8[0], k8[1]), vv = make_uint2(v8[0], v8[1]);
+    const size_t cache_base = (size_t)unit * (g + w) * d + (size_t)piece * 8;
+    if (j >= tn - w) {
+        const size_t dst = cache_base + (size_t)(g + (int)(P % w)) * d;
+        *reinterpret_cast<uint2 *>(kc + dst) = kk;
+        *reinterpret_cast<uint2 *>(vc + dst) = vv;
+    }
+    if (P < g) {
+        const size_t dst = cache_base + (size_t)P * d;
+        *reinterpret_cast<uint2 *>(kc + dst) = kk;
+        *reinterpret_cast<uint2 *>(vc + dst) = vv;
+    }
+}
+
+hipError_t launch_kv_append_fp8(void *kc, void *vc, const void *kn, const void *vn, const int64_t *pos,
+                                const float *ksc, const float *vsc, int batch, int heads, int tn, int d, int w,
+                                int g, bool bf16, hipStream_t stream) {
+    const long long total = (long long)batch * heads * tn * (d / 8);
+    const long long blocks = (total + 255) / 256;
+    if (bf16)
+        hipLaunchKernelGGL(kv_append_fp8_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, (uint8_t *)kc,
+                           (uint8_t *)vc, kn, vn, pos, ksc, vsc, heads, tn, d, w, g, total);
+    else
+        hipLaunchKernelGGL(kv_append_fp8_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, (uint8_t *)kc,
+                           (uint8_t *)vc, kn, vn, pos, ksc, vsc, heads, tn, d, w, g, total);
     return hipGetLastError();
 }
 

@@ -53,3 +53,21 @@ def decode_problem(batch: int, heads: int, d: int, rows: int, lo: int, hi: int, 
     gp = _gen(seed + 1, "cpu")
     pos = torch.randint(lo, hi + 1, (batch,), generator=gp, dtype=torch.int64).to(device)
     return q, kc, vc, pos
+
+
+def fp8_decode_problem(batch: int, heads: int, kv_heads: int, d: int, rows: int, lo: int, hi: int, q_dtype,
+                       seed: int, device="cpu"):
+    """(q [B,H,d], k_cache, v_cache [B,Hkv,rows,d] uint8, k_scale, v_scale [B,Hkv] fp32,
+    pos [B] int64 in [lo, hi]): cache bytes are torch's float8_e4m3fn casts of
+    N(0, 1) draws (so no NaN code appears), scales uniform in [0.25, 2]."""
+    g = _gen(seed, device)
+    q = torch.randn(batch, heads, d, generator=g, dtype=torch.float32, device=device).to(q_dtype)
+    kc = torch.randn(batch, kv_heads, rows, d, generator=g, dtype=torch.float32, device=device)
+    kc = kc.to(torch.float8_e4m3fn).view(torch.uint8)
+    vc = torch.randn(batch, kv_heads, rows, d, generator=g, dtype=torch.float32, device=device)
+    vc = vc.to(torch.float8_e4m3fn).view(torch.uint8)
+    ks = torch.rand(batch, kv_heads, generator=g, dtype=torch.float32, device=device) * 1.75 + 0.25
+    vs = torch.rand(batch, kv_heads, generator=g, dtype=torch.float32, device=device) * 1.75 + 0.25
+    gp = _gen(seed + 1, "cpu")
+    pos = torch.randint(lo, hi + 1, (batch,), generator=gp, dtype=torch.int64).to(device)
+    return q, kc, vc, ks, vs, pos

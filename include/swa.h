@@ -194,6 +194,37 @@ int swa_chunk_prefill_fwd(const void *q, const void *k_new, const void *v_new,
 int swa_lse_merge(const void *o_a, const float *lse_a, const void *o_b, const float *lse_b,
                   void *o, float *lse, long long rows, int d, swa_dtype_t dtype, hipStream_t stream);
 
+/*
+ * FP8 window KV cache ("Sliding Window and Sparse Attention, from Longformer
+ * to CSA2": s7 keeps the window KV in FP8; s10 glossary, E4M3: 1 sign, 4
+ * exponent, 3 mantissa bits).  Codes are OCP E4M3 (exponent bias 7, no
+ * infinities, S.1111.111 = NaN, largest finite 448), one byte per element,
+ * in the cache layout above: [batch][heads][g + w][d] bytes.  Each (batch,
+ * key/value head) has one fp32 scale for K and one for V (device arrays
+ * [batch][heads], positive and finite; the pages give no scale convention):
+ * a stored code c stands for scale * E4M3(c).
+ *
+ * swa_kv_append_fp8: as swa_kv_append, with every element x of k_new/v_new
+ * (dtype bf16 or fp32) stored as the code of x / scale (fp32 division,
+ * correctly rounded), rounded to the nearest code, ties to even, |x/scale|
+ * >= 448 saturated to 448, NaN kept NaN.
+ *
+ * swa_decode_fwd_fp8: as swa_decode_fwd_gqa over fp8 caches; q and o have
+ * the given dtype; scores use scale * k_scale * (q . code values), outputs
+ * v_scale * (weighted sum of code values); fp32 arithmetic.  Workspace size
+ * as swa_decode_workspace_bytes_gqa.  Errors as the bf16 calls (scales null
+ * or misaligned: SWA_EINVAL / SWA_EALIGN).
+ */
+int swa_kv_append_fp8(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
+                      const int64_t *pos, const float *k_scale, const float *v_scale,
+                      int batch, int heads, int t_new, int d, int w, int g,
+                      swa_dtype_t dtype, hipStream_t stream);
+int swa_decode_fwd_fp8(const void *q, const void *k_cache, const void *v_cache,
+                       const float *k_scale, const float *v_scale, const int64_t *pos,
+                       void *o, float *lse, int batch, int heads, int kv_heads, int d, int w, int g,
+                       float scale, float sink_bias, swa_dtype_t dtype,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static description of a status code. */
 const char *swa_strerror(int status);
 

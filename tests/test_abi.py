@@ -184,3 +184,40 @@ def _merge(**kw):
 ])
 def test_lse_merge_rejects(kw, want):
     assert _merge(**kw) == want
+
+
+def _append_fp8(**kw):
+    a = dict(kc=P, vc=P, kn=P, vn=P, pos=P, ks=P, vs=P, batch=1, heads=1, t=1, d=128, w=8, g=0, dtype=1)
+    a.update(kw)
+    return swa.lib().swa_kv_append_fp8(a["kc"], a["vc"], a["kn"], a["vn"], a["pos"], a["ks"], a["vs"], a["batch"],
+                                       a["heads"], a["t"], a["d"], a["w"], a["g"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(kc=None), EINVAL), (dict(ks=None), EINVAL), (dict(vs=None), EINVAL), (dict(batch=0), EINVAL),
+    (dict(t=-1), EINVAL), (dict(w=0), EINVAL), (dict(d=32), EUNSUP), (dict(dtype=3), EUNSUP),
+    (dict(ks=P + 2), EALIGN), (dict(pos=P + 4), EALIGN), (dict(kn=P + 8), EALIGN),
+    (dict(t=0), OK),
+])
+def test_kv_append_fp8_rejects(kw, want):
+    assert _append_fp8(**kw) == want
+
+
+def _decode_fp8(**kw):
+    a = dict(q=P, kc=P, vc=P, ks=P, vs=P, pos=P, o=P, lse=None, batch=64, heads=32, kv_heads=32, d=128, w=4096,
+             g=4, scale=0.125, bias=0.0, dtype=1, ws=None, wsb=0)
+    a.update(kw)
+    return swa.lib().swa_decode_fwd_fp8(a["q"], a["kc"], a["vc"], a["ks"], a["vs"], a["pos"], a["o"], a["lse"],
+                                        a["batch"], a["heads"], a["kv_heads"], a["d"], a["w"], a["g"], a["scale"],
+                                        a["bias"], a["dtype"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), EINVAL), (dict(ks=None), EINVAL), (dict(vs=None), EINVAL), (dict(kv_heads=3), EINVAL),
+    (dict(w=0), EINVAL), (dict(scale=-1.0), EINVAL), (dict(d=96), EUNSUP), (dict(dtype=2), EUNSUP),
+    (dict(vs=P + 1), EALIGN), (dict(kc=P + 8), EALIGN),
+    (dict(batch=1, heads=8, kv_heads=1), EWS),
+])
+def test_decode_fp8_rejects(kw, want):
+    assert _decode_fp8(**kw) == want
+

@@ -170,3 +170,26 @@ def test_decode_deterministic():
     b = swa.decode(q, kc, vc, pos, w=1024, g=4)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_decode_ignores_unwritten_rows(orc, dtype):
+    """Ring slots and sink rows never written hold NaN; decode at early
+    positions (ring not yet full, sinks still inside the window) stays finite
+    and equals the oracle."""
+    dev = _dev()
+    w, g, d = 64, 4, 128
+    positions = [0, 1, 5, 30, 62]
+    B, H = len(positions), 2
+    n = max(positions) + 1
+    kseq = synth.normal((B, H, n, d), seed=35, dtype=dtype, device="cpu")
+    vseq = synth.normal((B, H, n, d), seed=36, dtype=dtype, device="cpu")
+    q = synth.normal((B, H, d), seed=37, dtype=dtype, device="cpu").to(dev)
+    kc = torch.full((B, H, g + w, d), float("nan"), dtype=dtype, device=dev)
+    vc = torch.full_like(kc, float("nan"))
+    zero = torch.zeros(1, dtype=torch.int64, device=dev)
+    for b, p in enumerate(positions):
+        swa.kv_append(kc[b:b + 1], vc[b:b + 1], kseq[b:b + 1, :, :p + 1].contiguous().to(dev),
+                      vseq[b:b + 1, :, :p + 1].contiguous().to(dev), zero, w=w, g=g)
+    pos = torch.tensor(positions, dtype=torch.int64, device=dev)
+    _decode_vs_oracle(orc, q, kc, vc, pos, w, g, 0.0)
