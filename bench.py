@@ -57,6 +57,14 @@ CHUNK = {
     "chunk_prefill": (1, 32, 8, 4096, 16384, 128, 4096, 4, 0.0, 6),
 }
 
+PATTERN = {
+    # name: (batch, heads, n, d, kind, w, g, r, sink_bias, seed)
+    # every 4th key over a 4093-position span (a 1024-key window's cost)
+    "dilated_prefill": (1, 32, 16384, 128, "dilated", 1024, 0, 4, 0.0, 7),
+    # Mistral's window plus 4 sinks plus landmarks every 64 positions
+    "landmark_prefill": (1, 32, 16384, 128, "landmark", 4096, 4, 64, 0.0, 8),
+}
+
 # HBM traffic per launch measured with rocprofv3 counters (FETCH_SIZE and
 # WRITE_SIZE per dispatch, each scaled by what the same counter reads for a
 # plain device copy of known size, see --calibrate-copy), keyed by workload.
@@ -239,6 +247,85 @@ def cpu_baseline_chunk(name, budget_s=12.0):
                                         f"fp64, {dt:.1f} s"}
 
 
+def pattern_pairs(n: int, kind: str, w: int, g: int, r: int) -> int:
+    """Attended pairs of the fixed patterns, row by row."""
+    total = 0
+    for i in range(n):
+        if kind == "dilated":
+            total += min(w, i // r + 1)
+        else:  # window + sinks, then landmarks g <= j <= i - w
+            total += row_pairs(i, w, g)
+            if i - w >= g:
+                total += (i - w) // r - (g + r - 1) // r + 1
+    return total
+
+
+def bench_pattern(name, steps, warmup):
+    import torch
+
+    import block_sparse_causal_band_amd as swa
+    from block_sparse_causal_band_amd import synth
+
+    B, H, n, d, kind, w, g, r, beta, seed = PATTERN[name]
+    dev = torch.device("cuda")
+    q, k, v = synth.qkv(B, H, n, d, torch.bfloat16, seed=seed, device=dev)
+    o = torch.empty_like(q)
+    ws = torch.empty(max(swa.landmark_workspace_bytes(B, H, n, d, swa.SWA_BF16), 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        if kind == "dilated":
+            swa.dilated_prefill(q, k, v, w=w, r=r, out=o)
+        else:
+            swa.landmark_prefill(q, k, v, w=w, g=g, r=r, sink_bias=beta, out=o, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ms_step, ms_launch, per = _events_time(step, steps, stream)
+    flops = 4.0 * d * pattern_pairs(n, kind, w, g, r) * B * H
+    achieved = flops / (ms_launch * 1e-3) / 1e12
+    return {
+        "ms_per_step": ms_step,
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "dtype": "bf16",
+        "config": {"workload": name, "batch": B, "heads": H, "n": n, "d": d, "pattern": kind, "w": w, "g": g,
+                   "r": r, "sink_bias": beta, "band_flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": ("prefill_bf16_kernel<128,4,strided> (dilated classes)" if kind == "dilated" else
+                                "window prefill + landmark part + lse_merge (one call)"),
+                     "avg_launch_ms": ms_launch, "min_launch_ms": min(per)},
+    }
+
+
+def cpu_baseline_pattern(name, budget_s=12.0):
+    """The oracle's pattern rows (oracle/patterns.py, fp64 numpy) on the last
+    rows of one head of the same workload, until about budget_s seconds."""
+    import numpy as np
+    import torch
+
+    from block_sparse_causal_band_amd import synth
+    from oracle import patterns
+
+    B, H, n, d, kind, w, g, r, beta, seed = PATTERN[name]
+    q, k, v = synth.qkv(1, 1, n, d, torch.bfloat16, seed=seed, device="cpu")
+    qh, kh, vh = (t[0, 0].double().numpy() for t in (q, k, v))
+    done_pairs, done, t0 = 0, 0, time.perf_counter()
+    i = n - 1
+    while time.perf_counter() - t0 < budget_s and i >= 0:
+        rows = np.arange(max(0, i - 63), i + 1)
+        patterns.prefill(qh, kh, vh, kind, w=w, g=g, r=r, beta=beta, rows=rows)
+        for j in rows:
+            done_pairs += len(patterns.read_set(int(j), kind, w, g, r))
+        done += len(rows)
+        i -= 64
+    dt = time.perf_counter() - t0
+    return {"value": 4.0 * d * done_pairs / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} rows of one head of {name} (from the last row back), fp64 numpy, {dt:.1f} s"}
+
+
 def bench_decode(name, steps, warmup):
     import torch
 
@@ -391,7 +478,7 @@ def main():
     # the clock settles over the first ~25 launches of a busy kernel (power
     # management); the default warmup keeps the timed launches past that
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="mistral_prefill", choices=sorted(PREFILL) + sorted(DECODE) + sorted(CHUNK))
+    ap.add_argument("--workload", default="mistral_prefill", choices=sorted(PREFILL) + sorted(DECODE) + sorted(CHUNK) + sorted(PATTERN))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode figures on a prefill line")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -415,6 +502,8 @@ def main():
         r = bench_prefill(args.workload, args.steps, args.warmup)
     elif args.workload in CHUNK:
         r = bench_chunk(args.workload, args.steps, args.warmup)
+    elif args.workload in PATTERN:
+        r = bench_pattern(args.workload, args.steps, args.warmup)
     else:
         r = bench_decode(args.workload, args.steps, args.warmup)
     line = {
@@ -444,6 +533,8 @@ def main():
             line["cpu_baseline"] = cpu_baseline_prefill(args.workload)
         elif args.workload in CHUNK:
             line["cpu_baseline"] = cpu_baseline_chunk(args.workload)
+        elif args.workload in PATTERN:
+            line["cpu_baseline"] = cpu_baseline_pattern(args.workload)
         else:
             line["cpu_baseline"] = cpu_baseline_decode(args.workload)
     print(json.dumps(line), flush=True)

@@ -6,6 +6,7 @@ behind the C ABI of include/swa.h); this package is its thin Python binding.
     from block_sparse_causal_band_amd import prefill, kv_append, decode
     from block_sparse_causal_band_amd import chunk_prefill, lse_merge
     from block_sparse_causal_band_amd import kv_append_fp8, decode_fp8
+    from block_sparse_causal_band_amd import dilated_prefill, landmark_prefill
 
 Importing the package does not load the library; the first call does, and
 raises if it is not built (``python -m block_sparse_causal_band_amd.build``).
@@ -19,8 +20,11 @@ from .binding import (  # noqa: F401
     decode,
     decode_fp8,
     decode_workspace_bytes,
+    dilated_prefill,
     kv_append,
     kv_append_fp8,
+    landmark_prefill,
+    landmark_workspace_bytes,
     lib,
     lse_merge,
     prefill,

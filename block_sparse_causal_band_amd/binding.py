@@ -69,6 +69,13 @@ def lib() -> ctypes.CDLL:
         L.swa_decode_fwd_fp8.argtypes = ([_vp] * 8 + [_int] * 6 + [ctypes.c_float] * 2 + [_int, _vp, ctypes.c_size_t,
                                                                                            _vp])
         L.swa_decode_fwd_fp8.restype = _int
+        L.swa_dilated_prefill_fwd.argtypes = [_vp] * 5 + [_int] * 7 + [ctypes.c_float, _int, _vp]
+        L.swa_dilated_prefill_fwd.restype = _int
+        L.swa_landmark_prefill_fwd.argtypes = ([_vp] * 5 + [_int] * 8 + [ctypes.c_float] * 2 +
+                                               [_int, _vp, ctypes.c_size_t, _vp])
+        L.swa_landmark_prefill_fwd.restype = _int
+        L.swa_landmark_workspace_bytes.argtypes = [_int] * 5
+        L.swa_landmark_workspace_bytes.restype = ctypes.c_size_t
         L.swa_lse_merge.argtypes = [_vp] * 6 + [ctypes.c_longlong, _int, _int, _vp]
         L.swa_lse_merge.restype = _int
         L.swa_strerror.argtypes = [_int]
@@ -270,6 +277,64 @@ def decode(q, k_cache, v_cache, pos, w: int, g: int = 0, scale: float | None = N
                                   _stream(q))
     if rc != 0:
         raise SwaError(rc, "swa_decode_fwd_gqa")
+    return (o, lse) if return_lse else o
+
+
+def _prefill_shapes(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(t, name)
+    _need(q.dim() == 4 and k.dim() == 4 and k.shape == v.shape, "q, k, v must be 4-d, k and v one shape")
+    _need(q.shape[0] == k.shape[0] and q.shape[2:] == k.shape[2:],
+          "q [batch, heads, n, d] and k, v [batch, kv_heads, n, d] must agree on batch, n, d")
+    _need(q.dtype == k.dtype == v.dtype, "q, k, v must share one dtype")
+    B, H, n, d = q.shape
+    return B, H, k.shape[1], n, d
+
+
+def dilated_prefill(q, k, v, w: int, r: int, scale: float | None = None, return_lse: bool = False, out=None):
+    """Dilated causal window: query i reads keys i, i-r, ..., i-(w-1)r."""
+    import torch
+
+    B, H, Hkv, n, d = _prefill_shapes(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    _dev_tensor(o, "out")
+    _need(o.shape == q.shape and o.dtype == q.dtype, "out must match q")
+    lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device) if return_lse else None
+    rc = lib().swa_dilated_prefill_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                       lse.data_ptr() if lse is not None else None, B, H, Hkv, n, d, int(w), int(r),
+                                       float(scale), _dtype_code(q), _stream(q))
+    if rc != 0:
+        raise SwaError(rc, "swa_dilated_prefill_fwd")
+    return (o, lse) if return_lse else o
+
+
+def landmark_workspace_bytes(batch: int, heads: int, n: int, d: int, dtype_code: int) -> int:
+    return int(lib().swa_landmark_workspace_bytes(batch, heads, n, d, dtype_code))
+
+
+def landmark_prefill(q, k, v, w: int, r: int, g: int = 0, scale: float | None = None, sink_bias: float = 0.0,
+                     return_lse: bool = False, out=None, workspace=None):
+    """Window of w, sinks 0..g-1 and landmarks every r positions, each key once."""
+    import torch
+
+    B, H, Hkv, n, d = _prefill_shapes(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    _dev_tensor(o, "out")
+    _need(o.shape == q.shape and o.dtype == q.dtype, "out must match q")
+    lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device) if return_lse else None
+    need = landmark_workspace_bytes(B, H, n, d, _dtype_code(q))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    rc = lib().swa_landmark_prefill_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                        lse.data_ptr() if lse is not None else None, B, H, Hkv, n, d, int(w), int(g),
+                                        int(r), float(scale), float(sink_bias), _dtype_code(q), workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(), _stream(q))
+    if rc != 0:
+        raise SwaError(rc, "swa_landmark_prefill_fwd")
     return (o, lse) if return_lse else o
 
 

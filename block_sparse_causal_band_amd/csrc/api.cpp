@@ -23,6 +23,12 @@ hipError_t launch_chunk_prefill(const void *q, const void *k_new, const void *v_
                                 const void *v_cache, const int64_t *pos, void *o, float *lse, int batch, int heads,
                                 int kv_heads, int t, int d, int w, int g, float scale, float sink_bias, int part,
                                 bool bf16, hipStream_t stream);
+hipError_t launch_dilated_prefill(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
+                                  int heads, int kv_heads, int n, int d, int w, int r, float scale, bool bf16,
+                                  hipStream_t stream);
+hipError_t launch_landmark_part(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
+                                int heads, int kv_heads, int n, int d, int w, int g, int r, float scale, bool bf16,
+                                hipStream_t stream);
 hipError_t launch_kv_append_fp8(void *kc, void *vc, const void *kn, const void *vn, const int64_t *pos,
                                 const float *ksc, const float *vsc, int batch, int heads, int tn, int d, int w,
                                 int g, bool bf16, hipStream_t stream);
@@ -106,6 +112,72 @@ int swa_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v
     if (blocks > INT_MAX) return SWA_EINVAL;
     return status_of(swa::launch_kv_append(k_cache, v_cache, k_new, v_new, pos, batch, heads, t_new, d, w, g,
                                            dtype == SWA_BF16, stream));
+}
+
+// shared checks of the whole-sequence prefill forms
+static int check_prefill(const void *q, const void *k, const void *v, const void *o, const float *lse, int batch,
+                         int heads, int kv_heads, int n, int d, int w, int g, float scale, float sink_bias,
+                         swa_dtype_t dtype, int units_mul) {
+    if (!q || !k || !v || !o) return SWA_EINVAL;
+    if (batch < 1 || heads < 1 || n < 1 || w < 1 || g < 0) return SWA_EINVAL;
+    if (kv_heads < 1 || kv_heads > heads || heads % kv_heads != 0) return SWA_EINVAL;
+    if (!std::isfinite(scale) || !(scale > 0.f) || !std::isfinite(sink_bias)) return SWA_EINVAL;
+    int st = check_dtype_d(dtype, d);
+    if (st != SWA_OK) return st;
+    const int bq = swa::prefill_bq(dtype == SWA_BF16);
+    if (n > INT_MAX - bq) return SWA_EINVAL;
+    const long long units = (long long)batch * heads * units_mul;
+    const long long nqb = (n + bq - 1) / bq;
+    if (units * nqb > INT_MAX) return SWA_EINVAL;
+    const long long row_bytes = (long long)d * (dtype == SWA_BF16 ? 2 : 4);
+    if ((long long)n * row_bytes >= (1LL << 32)) return SWA_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned4(lse)))
+        return SWA_EALIGN;
+    return SWA_OK;
+}
+
+int swa_dilated_prefill_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int batch, int heads,
+                            int kv_heads, int n, int d, int w, int r, float scale, swa_dtype_t dtype,
+                            hipStream_t stream) {
+    if (r < 1) return SWA_EINVAL;
+    int st = check_prefill(q, k, v, o, lse, batch, heads, kv_heads, n, d, w, 0, scale, 0.f, dtype, r);
+    if (st != SWA_OK) return st;
+    return status_of(swa::launch_dilated_prefill(q, k, v, o, lse, batch, heads, kv_heads, n, d, w, r, scale,
+                                                 dtype == SWA_BF16, stream));
+}
+
+size_t swa_landmark_workspace_bytes(int batch, int heads, int n, int d, swa_dtype_t dtype) {
+    if (batch < 1 || heads < 1 || n < 1 || (d != 64 && d != 128) || (dtype != SWA_F32 && dtype != SWA_BF16))
+        return 0;
+    const size_t rows = (size_t)batch * heads * n;
+    const size_t ob = (rows * d * (dtype == SWA_BF16 ? 2 : 4) + 255) / 256 * 256;
+    const size_t lb = (rows * 4 + 255) / 256 * 256;
+    return ob + 2 * lb;
+}
+
+int swa_landmark_prefill_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int batch, int heads,
+                             int kv_heads, int n, int d, int w, int g, int r, float scale, float sink_bias,
+                             swa_dtype_t dtype, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (r < 1) return SWA_EINVAL;
+    int st = check_prefill(q, k, v, o, lse, batch, heads, kv_heads, n, d, w, g, scale, sink_bias, dtype, 1);
+    if (st != SWA_OK) return st;
+    const size_t need = swa_landmark_workspace_bytes(batch, heads, n, d, dtype);
+    if (!workspace || workspace_bytes < need) return SWA_EWORKSPACE;
+    if (!aligned16(workspace)) return SWA_EALIGN;
+    const bool bf16 = dtype == SWA_BF16;
+    const size_t rows = (size_t)batch * heads * n;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    void *o_b = ws;
+    float *lse_a = reinterpret_cast<float *>(ws + (rows * d * (bf16 ? 2 : 4) + 255) / 256 * 256);
+    float *lse_b = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(lse_a) + (rows * 4 + 255) / 256 * 256);
+    // window and sinks into o, landmarks into the workspace, then the LSE merge into o
+    hipError_t e = swa::launch_prefill(q, k, v, o, lse_a, batch, heads, kv_heads, n, d, w, g, scale, sink_bias, bf16,
+                                       stream);
+    if (e == hipSuccess)
+        e = swa::launch_landmark_part(q, k, v, o_b, lse_b, batch, heads, kv_heads, n, d, w, g, r, scale, bf16,
+                                      stream);
+    if (e == hipSuccess) e = swa::launch_lse_merge(o, lse_a, o_b, lse_b, o, lse, (long)rows, d, bf16, stream);
+    return status_of(e);
 }
 
 int swa_chunk_prefill_fwd(const void *q, const void *k_new, const void *v_new, const void *k_cache,

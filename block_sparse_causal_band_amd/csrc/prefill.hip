@@ -85,12 +85,30 @@ __device__ __forceinline__ size_t kv_offset(int unit, int heads, int kv_heads, i
 // neither were evicted and are never attended; their loads land on some
 // finite cache row or read as zero past the cache and are masked.
 // part: 0 = every key, 1 = cache keys only (s < p0), 2 = chunk keys only.
-struct ChunkArgs {
-    const void *kc;        // K cache [batch][kv_heads][g + w][d]
-    const void *vc;        // V cache, same layout
-    const int64_t *pos;    // p0 of each batch entry
-    int part;
+//
+// Strided fixed patterns on the same tiles ("Sliding Window and Sparse
+// Attention, from Longformer to CSA2", s2 dilated windows and s4 block-sparse
+// substrate; "Local and Sparse Attention: Reading Fewer Token Positions",
+// Figure 2 landmarks):
+//  * dilated (mode 1): query i reads keys i, i-r, ..., i-(w-1)r.  The rows of
+//    one residue class c = i mod r form an ordinary causal window of w over
+//    the subsequence c, c+r, c+2r, ...: the grid runs one unit per (batch,
+//    head, class) on rows strided by r, with class-local positions.
+//  * landmark part (mode 2): query i reads the landmarks j = k r that lie
+//    below its window and are not sinks (g <= j <= i-w); over the K/V rows
+//    strided by r that is the compact index range ceil(g/r) <= k <=
+//    floor((i-w)/r).  The window-and-sinks part is an ordinary launch; the
+//    two parts merge by LSE.
+enum { kPlain = 0, kChunk = 1, kStrided = 2 };
+struct PathArgs {
+    const void *kc;        // chunk: K cache [batch][kv_heads][g + w][d]
+    const void *vc;        // chunk: V cache, same layout
+    const int64_t *pos;    // chunk: p0 of each batch entry
+    int part;              // chunk: which keys
+    int r;                 // strided: the stride
+    int mode;              // strided: 1 dilated, 2 landmark part
 };
+constexpr int kNoWindow = 1 << 30;  // a window wider than any sequence
 
 // Cache row of key position s < p0 (s >= 0).
 __device__ __forceinline__ int cache_row(int s, int p0, int w, int g) {
@@ -155,13 +173,14 @@ __device__ __forceinline__ void update_max(const f32x16 (&s)[2], float &m_run, f
 }
 
 // Normalise and store O (and LSE) of this lane's query row.
+// Query row qi is row qi * rs of O and of lse.
 template <typename T, int D>
 __device__ __forceinline__ void store_rows(const f32x16 (&oacc)[D / 32], float m_run, float l_run, int qi, int n,
-                                           int lh, T *O, float *lse, float scale) {
+                                           int lh, T *O, float *lse, float scale, int rs = 1) {
     const float l_tot = half_swap_sum(l_run);
     const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
     if (qi >= n) return;
-    T *orow = O + (size_t)qi * D;
+    T *orow = O + (size_t)qi * rs * D;
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
@@ -175,7 +194,7 @@ __device__ __forceinline__ void store_rows(const f32x16 (&oacc)[D / 32], float m
                 *reinterpret_cast<float4 *>(orow + c) = make_float4(x0, x1, x2, x3);
             }
         }
-    if (lse != nullptr && lh == 0) lse[qi] = m_run * scale + logf(l_tot);
+    if (lse != nullptr && lh == 0) lse[(size_t)qi * rs] = m_run * scale + logf(l_tot);
 }
 
 // ---------------------------------------------------------------------------
@@ -198,14 +217,15 @@ struct Bf16Tile {
     }
 };
 
-// CHUNK: the queries are a chunk of n positions starting at p0 = pos[b] and
-// the keys come from the chunk and the cache (ChunkArgs); otherwise q, k, v
-// are whole sequences of n positions and p0 = 0.
-template <int D, int WAVES, bool CHUNK>
+// KIND kChunk: the queries are a chunk of n positions starting at p0 =
+// pos[b] and the keys come from the chunk and the cache; kStrided: a strided
+// pattern (PathArgs); kPlain: q, k, v are whole sequences of n positions.
+template <int D, int WAVES, int KIND>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp, const uint16_t *__restrict__ vp,
     uint16_t *__restrict__ op, float *__restrict__ lsep, int n, int nqb, int w, int g, float c2, float scale,
-    float bias_raw, int total_wg, int heads, int kv_heads, ChunkArgs ca) {
+    float bias_raw, int total_wg, int heads, int kv_heads, PathArgs ca) {
+    constexpr bool CHUNK = (KIND == kChunk), STRIDED = (KIND == kStrided);
     using L = Bf16Tile<D, WAVES>;
     constexpr int BQ = 32 * WAVES;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * L::kStageBytes];
@@ -218,16 +238,31 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
 
     int unit, qb;
     workgroup_order(blockIdx.x, total_wg, nqb, &unit, &qb);
+    // strided patterns: query row i of this unit is row oq + i sq of q and o,
+    // key index k is row okv + k skv of k and v; nq query rows
+    int nq = n, sq = 1, oq = 0, skv = 1, okv = 0;
+    if constexpr (STRIDED) {
+        if (ca.mode == 1) {
+            const int cls = unit % ca.r;
+            unit /= ca.r;
+            nq = (n - cls + ca.r - 1) / ca.r;
+            sq = ca.r;
+            oq = cls;
+            okv = cls;
+        }
+        skv = ca.r;
+    }
     const size_t base = (size_t)unit * n * D;  // q and o of (batch, head)
     const uint16_t *Q = qp + base;
     const uint16_t *K = kp + kv_offset(unit, heads, kv_heads, n, D);
     const uint16_t *V = vp + kv_offset(unit, heads, kv_heads, n, D);
 
-    const int q0 = qb * BQ;  // rows of this block: q0 .. q1 (< n)
-    const int q1 = min(q0 + BQ, n) - 1;
+    const int q0 = qb * BQ;  // rows of this block: q0 .. q1 (< nq)
+    const int q1 = min(q0 + BQ, nq) - 1;
     const int qi = q0 + wave * 32 + lr;
+    if (STRIDED && q0 >= nq) return;  // a residue class shorter than the longest one
     // positions: query row r is at p0 + r; keys are attended in [klo, khi)
-    int p0 = 0, klo = 0, khi = n;
+    int p0 = 0, klo = 0, khi = n, wq = w;
     const uint16_t *KC = nullptr, *VC = nullptr;
     if constexpr (CHUNK) {
         const int b = unit / heads;
@@ -249,16 +284,34 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
         KC = reinterpret_cast<const uint16_t *>(ca.kc) + coff;
         VC = reinterpret_cast<const uint16_t *>(ca.vc) + coff;
     }
-    const int qa = p0 + qi;  // position of this lane's query row
-    const BandRange band = band_range(p0 + q0, p0 + q1, w, g, kBK);
+    if constexpr (STRIDED) {
+        if (ca.mode == 1) {
+            khi = nq;  // class-local positions, an ordinary window
+        } else {
+            khi = (n + ca.r - 1) / ca.r;  // landmarks k r < n
+            klo = (g + ca.r - 1) / ca.r;  // landmarks below g are sinks of the other part
+            wq = kNoWindow;
+            g = 0;
+        }
+    }
+    // key position bound of query row r (the causal limit j <= qpos(r))
+    auto qpos = [&](int r) -> int {
+        if constexpr (STRIDED) {
+            if (ca.mode == 2) return (r >= w) ? (r - w) / ca.r : -1;
+        }
+        return p0 + r;
+    };
+    const int qa = qpos(qi);  // position of this lane's query row
+    const BandRange band = band_range(qpos(q0), qpos(q1), wq, g, kBK);
     const int ntiles = band.count();
     const float tau = 8.f / c2;
 
     // ---- Q of this wave's 32 rows as the B operand (kept in VGPRs) ----
     bf16x8 qf[D / 16];
     {
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + (size_t)q0 * D, (uint32_t)(n - q0) * L::kRowBytes);
-        const uint32_t rowoff = (uint32_t)(wave * 32 + lr) * L::kRowBytes;
+        const int qr0 = oq + q0 * sq;  // first row of this block in q
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + (size_t)qr0 * D, (uint32_t)(n - qr0) * L::kRowBytes);
+        const uint32_t rowoff = (uint32_t)((wave * 32 + lr) * sq) * L::kRowBytes;
 #pragma unroll
         for (int c = 0; c < D / 16; ++c)
             qf[c] = __builtin_bit_cast(bf16x8, buffer_load16(rq, rowoff + (16 * c + 8 * lh) * 2));
@@ -278,8 +331,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
         const int pos = lane & 3;
         const int ck = (m >> 2) * 4 + (pos ^ ((key >> 2) & 3));
         const int cv = (m >> 2) * 4 + pos;
-        dma_k[i] = key * L::kRowBytes + 16 * ck;
-        dma_v[i] = key * L::kRowBytes + 16 * cv;
+        dma_k[i] = key * skv * L::kRowBytes + 16 * ck;
+        dma_v[i] = key * skv * L::kRowBytes + 16 * cv;
     }
     uint8_t *const kbuf = smem;                       // K buffers 0, 1
     uint8_t *const vbuf = smem + 2 * L::kTileBytes;   // V buffers 0, 1
@@ -294,7 +347,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
         const uint16_t *src = is_k ? K : V;
         const uint32_t *offs = is_k ? dma_k : dma_v;
         if constexpr (!CHUNK) {
-            dma_rows(src, offs, k0, n, dst);
+            dma_rows(src, offs, okv + k0 * skv, n, dst);
         } else {
             const uint16_t *cache = is_k ? KC : VC;
             if (k0 >= p0) {
@@ -400,7 +453,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
 #pragma unroll
         for (int j = 0; j < NS; ++j) kf[j] = kfrag(j);
 
-        if constexpr (MASKED) mask_tile<CHUNK>(s_cur, qa, k0, lh, khi, w, g, bias_raw, klo);
+        if constexpr (MASKED) mask_tile<CHUNK || STRIDED>(s_cur, qa, k0, lh, khi, wq, g, bias_raw, klo);
         update_max(s_cur, m_run, negm, l_run, oacc, c2, tau);
 
         // The rest of the tile is two interleaved streams, in a fixed order
@@ -472,14 +525,14 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     // workgroup's block cut a single wave's rows in fewer tiles.
     int t_lo = 0, t_hi = ntiles;  // a wave entirely past n keeps all tiles unmasked (nothing is stored)
     const int qw0 = q0 + wave * 32;
-    if (qw0 < n) full_range(band, p0 + qw0, p0 + min(qw0 + 31, n - 1), khi, w, g, kBK, &t_lo, &t_hi, klo);
+    if (qw0 < nq) full_range(band, qpos(qw0), qpos(min(qw0 + 31, nq - 1)), khi, wq, g, kBK, &t_lo, &t_hi, klo);
     int t = 0;
     for (; t < t_lo; ++t) do_tile(t, std::true_type{});
     for (; t < t_hi; ++t) do_tile(t, std::false_type{});
     for (; t < ntiles; ++t) do_tile(t, std::true_type{});
 
-    store_rows<uint16_t, D>(oacc, m_run, l_run, qi, n, lh, op + base, lsep ? lsep + (size_t)unit * n : nullptr,
-                            scale);
+    store_rows<uint16_t, D>(oacc, m_run, l_run, qi, nq, lh, op + base + (size_t)oq * D,
+                            lsep ? lsep + (size_t)unit * n + oq : nullptr, scale, sq);
 }
 
 // ---------------------------------------------------------------------------
@@ -497,17 +550,18 @@ struct F32Cfg {
     static_assert(kBK * kCPR % kThreads == 0 && (kBK / 4) * kCPR % kThreads == 0, "tile split");
 };
 
-// Where the fp32 loader finds key position s: whole-sequence rows (p0 = 0,
-// rows >= n read as zero), or chunk / cache rows as in the bf16 path.
+// Where the fp32 loader finds key index s: row okv + s skv of the sequence
+// (rows >= n read as zero), or chunk / cache rows as in the bf16 path.
 struct F32KeyRows {
     const float *k, *v;    // sequence or chunk rows
     const float *kc, *vc;  // cache rows (chunked prefill only)
     int n, p0, w, g;
     bool chunk;
+    int skv, okv;          // strided patterns
     __device__ __forceinline__ uint4 load(bool is_k, int s, int col_byte, int d) const {
         if (!chunk || s >= p0) {
             const __amdgpu_buffer_rsrc_t r = make_rsrc(is_k ? k : v, (uint32_t)n * d * 4);
-            return buffer_load16(r, (uint32_t)(s - p0) * d * 4 + col_byte);
+            return buffer_load16(r, (uint32_t)(okv + (s - p0) * skv) * d * 4 + col_byte);
         }
         const __amdgpu_buffer_rsrc_t r = make_rsrc(is_k ? kc : vc, (uint32_t)(g + w) * d * 4);
         return buffer_load16(r, (uint32_t)cache_row(s, p0, w, g) * d * 4 + col_byte);
@@ -556,11 +610,12 @@ struct F32TileLoader {
     }
 };
 
-template <int D, bool CHUNK>
+template <int D, int KIND>
 __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
     const float *__restrict__ qp, const float *__restrict__ kp, const float *__restrict__ vp,
     float *__restrict__ op, float *__restrict__ lsep, int n, int nqb, int w, int g, float c2, float scale,
-    float bias_raw, int total_wg, int heads, int kv_heads, ChunkArgs ca) {
+    float bias_raw, int total_wg, int heads, int kv_heads, PathArgs ca) {
+    constexpr bool CHUNK = (KIND == kChunk), STRIDED = (KIND == kStrided);
     using C = F32Cfg<D>;
     __shared__ __attribute__((aligned(16))) float smem[2 * C::kStage];
 
@@ -572,16 +627,29 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
 
     int unit, qb;
     workgroup_order(blockIdx.x, total_wg, nqb, &unit, &qb);
+    int nq = n, sq = 1, oq = 0, skv = 1, okv = 0;  // strided patterns, as in the bf16 kernel
+    if constexpr (STRIDED) {
+        if (ca.mode == 1) {
+            const int cls = unit % ca.r;
+            unit /= ca.r;
+            nq = (n - cls + ca.r - 1) / ca.r;
+            sq = ca.r;
+            oq = cls;
+            okv = cls;
+        }
+        skv = ca.r;
+    }
     const size_t base = (size_t)unit * n * D;  // q and o of (batch, head)
     const float *Q = qp + base;
     const float *K = kp + kv_offset(unit, heads, kv_heads, n, D);
     const float *V = vp + kv_offset(unit, heads, kv_heads, n, D);
 
     const int q0 = qb * kBQ;
-    const int q1 = min(q0 + kBQ, n) - 1;
+    const int q1 = min(q0 + kBQ, nq) - 1;
     const int qi = q0 + wave * 32 + lr;
-    F32KeyRows src{K, V, nullptr, nullptr, n, 0, w, g, CHUNK};
-    int p0 = 0, klo = 0, khi = n;
+    if (STRIDED && q0 >= nq) return;
+    F32KeyRows src{K, V, nullptr, nullptr, n, 0, w, g, CHUNK, skv, okv};
+    int p0 = 0, klo = 0, khi = n, wq = w;
     if constexpr (CHUNK) {
         const int b = unit / heads;
         const int64_t pb = ca.pos[b];
@@ -604,16 +672,33 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
         src.vc = reinterpret_cast<const float *>(ca.vc) + coff;
         src.p0 = p0;
     }
-    const int qa = p0 + qi;
-    const BandRange band = band_range(p0 + q0, p0 + q1, w, g, kBK);
+    if constexpr (STRIDED) {
+        if (ca.mode == 1) {
+            khi = nq;
+        } else {
+            khi = (n + ca.r - 1) / ca.r;
+            klo = (g + ca.r - 1) / ca.r;
+            wq = kNoWindow;
+            g = 0;
+        }
+    }
+    auto qpos = [&](int r) -> int {
+        if constexpr (STRIDED) {
+            if (ca.mode == 2) return (r >= w) ? (r - w) / ca.r : -1;
+        }
+        return p0 + r;
+    };
+    const int qa = qpos(qi);
+    const BandRange band = band_range(qpos(q0), qpos(q1), wq, g, kBK);
     const int ntiles = band.count();
     const float tau = 8.f / c2;
 
     // Q as the B operand of 32x32x2 MFMAs: lane half lh holds d = 2c + lh
     float qf[D / 2];
     {
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + (size_t)q0 * D, (uint32_t)(n - q0) * D * 4);
-        const uint32_t rowoff = (uint32_t)(wave * 32 + lr) * D * 4;
+        const int qr0 = oq + q0 * sq;
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + (size_t)qr0 * D, (uint32_t)(n - qr0) * D * 4);
+        const uint32_t rowoff = (uint32_t)((wave * 32 + lr) * sq) * D * 4;
 #pragma unroll
         for (int c4 = 0; c4 < D / 8; ++c4) {
             const uint4 a = buffer_load16(rq, rowoff + (8 * c4) * 4);
@@ -654,7 +739,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
             for (int c = 0; c < D / 2; ++c)
                 s[sb] = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * c], qf[c], s[sb], 0, 0, 0);
         }
-        if constexpr (MASKED) mask_tile<CHUNK>(s, qa, k0, lh, khi, w, g, bias_raw, klo);
+        if constexpr (MASKED) mask_tile<CHUNK || STRIDED>(s, qa, k0, lh, khi, wq, g, bias_raw, klo);
         update_max(s, m_run, negm, l_run, oacc, c2, tau);
 
         float lsum = 0.f;
@@ -685,51 +770,55 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
     };
 
     int t_lo, t_hi;
-    full_range(band, p0 + q0, p0 + q1, khi, w, g, kBK, &t_lo, &t_hi, klo);
+    full_range(band, qpos(q0), qpos(q1), khi, wq, g, kBK, &t_lo, &t_hi, klo);
     int t = 0, stage = 0;
     for (; t < t_lo; ++t, stage ^= 1) do_tile(t, stage, std::true_type{});
     for (; t < t_hi; ++t, stage ^= 1) do_tile(t, stage, std::false_type{});
     for (; t < ntiles; ++t, stage ^= 1) do_tile(t, stage, std::true_type{});
 
-    store_rows<float, D>(oacc, m_run, l_run, qi, n, lh, op + base, lsep ? lsep + (size_t)unit * n : nullptr, scale);
+    store_rows<float, D>(oacc, m_run, l_run, qi, nq, lh, op + base + (size_t)oq * D,
+                         lsep ? lsep + (size_t)unit * n + oq : nullptr, scale, sq);
 }
 
 // ---------------------------------------------------------------------------
 // Query rows per workgroup (the prefill grid is units x ceil(n / rows)).
 int prefill_rows_per_workgroup(bool bf16) { return bf16 ? 32 * kWaves16 : kBQ; }
 
-// Host launchers (validated arguments only).
-template <bool CHUNK>
+// Host launchers (validated arguments only).  units_mul: grid units per
+// (batch, head) (the residue classes of a dilated launch); nq_max: query rows
+// of the longest unit.
+template <int KIND>
 static hipError_t launch_prefill_t(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
                                    int heads, int kv_heads, int n, int d, int w, int g, float scale,
-                                   float sink_bias, bool bf16, ChunkArgs ca, hipStream_t stream) {
-    const int units = batch * heads;
+                                   float sink_bias, bool bf16, PathArgs ca, int units_mul, int nq_max,
+                                   hipStream_t stream) {
+    const int units = batch * heads * units_mul;
     const float c2 = (float)((double)scale * kLog2e);
     const float bias_raw = (float)((double)sink_bias / (double)scale);
     if (bf16) {
         const int bq = 32 * kWaves16;
-        const int nqb = (n + bq - 1) / bq;
+        const int nqb = (nq_max + bq - 1) / bq;
         const int total = units * nqb;
         const dim3 grid(total), block(64 * kWaves16);
         const uint16_t *qq = (const uint16_t *)q, *kk = (const uint16_t *)k, *vv = (const uint16_t *)v;
         uint16_t *oo = (uint16_t *)o;
         if (d == 128)
-            hipLaunchKernelGGL((prefill_bf16_kernel<128, kWaves16, CHUNK>), grid, block, 0, stream, qq, kk, vv, oo,
+            hipLaunchKernelGGL((prefill_bf16_kernel<128, kWaves16, KIND>), grid, block, 0, stream, qq, kk, vv, oo,
                                lse, n, nqb, w, g, c2, scale, bias_raw, total, heads, kv_heads, ca);
         else
-            hipLaunchKernelGGL((prefill_bf16_kernel<64, kWaves16, CHUNK>), grid, block, 0, stream, qq, kk, vv, oo,
+            hipLaunchKernelGGL((prefill_bf16_kernel<64, kWaves16, KIND>), grid, block, 0, stream, qq, kk, vv, oo,
                                lse, n, nqb, w, g, c2, scale, bias_raw, total, heads, kv_heads, ca);
     } else {
-        const int nqb = (n + kBQ - 1) / kBQ;
+        const int nqb = (nq_max + kBQ - 1) / kBQ;
         const int total = units * nqb;
         const dim3 grid(total), block(kThreads);
         const float *qq = (const float *)q, *kk = (const float *)k, *vv = (const float *)v;
         float *oo = (float *)o;
         if (d == 128)
-            hipLaunchKernelGGL((prefill_f32_kernel<128, CHUNK>), grid, block, 0, stream, qq, kk, vv, oo, lse, n, nqb,
+            hipLaunchKernelGGL((prefill_f32_kernel<128, KIND>), grid, block, 0, stream, qq, kk, vv, oo, lse, n, nqb,
                                w, g, c2, scale, bias_raw, total, heads, kv_heads, ca);
         else
-            hipLaunchKernelGGL((prefill_f32_kernel<64, CHUNK>), grid, block, 0, stream, qq, kk, vv, oo, lse, n, nqb,
+            hipLaunchKernelGGL((prefill_f32_kernel<64, KIND>), grid, block, 0, stream, qq, kk, vv, oo, lse, n, nqb,
                                w, g, c2, scale, bias_raw, total, heads, kv_heads, ca);
     }
     return hipGetLastError();
@@ -738,16 +827,34 @@ static hipError_t launch_prefill_t(const void *q, const void *k, const void *v, 
 hipError_t launch_prefill(const void *q, const void *k, const void *v, void *o, float *lse, int batch, int heads,
                           int kv_heads, int n, int d, int w, int g, float scale, float sink_bias, bool bf16,
                           hipStream_t stream) {
-    return launch_prefill_t<false>(q, k, v, o, lse, batch, heads, kv_heads, n, d, w, g, scale, sink_bias, bf16,
-                                   ChunkArgs{nullptr, nullptr, nullptr, 0}, stream);
+    return launch_prefill_t<kPlain>(q, k, v, o, lse, batch, heads, kv_heads, n, d, w, g, scale, sink_bias, bf16,
+                                    PathArgs{nullptr, nullptr, nullptr, 0, 1, 0}, 1, n, stream);
 }
 
 hipError_t launch_chunk_prefill(const void *q, const void *k_new, const void *v_new, const void *k_cache,
                                 const void *v_cache, const int64_t *pos, void *o, float *lse, int batch, int heads,
                                 int kv_heads, int t, int d, int w, int g, float scale, float sink_bias, int part,
                                 bool bf16, hipStream_t stream) {
-    return launch_prefill_t<true>(q, k_new, v_new, o, lse, batch, heads, kv_heads, t, d, w, g, scale, sink_bias,
-                                  bf16, ChunkArgs{k_cache, v_cache, pos, part}, stream);
+    return launch_prefill_t<kChunk>(q, k_new, v_new, o, lse, batch, heads, kv_heads, t, d, w, g, scale, sink_bias,
+                                    bf16, PathArgs{k_cache, v_cache, pos, part, 1, 0}, 1, t, stream);
+}
+
+// Dilated window: r residue classes per (batch, head), each an ordinary
+// window of w over its strided rows (no sinks).
+hipError_t launch_dilated_prefill(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
+                                  int heads, int kv_heads, int n, int d, int w, int r, float scale, bool bf16,
+                                  hipStream_t stream) {
+    return launch_prefill_t<kStrided>(q, k, v, o, lse, batch, heads, kv_heads, n, d, w, 0, scale, 0.f, bf16,
+                                      PathArgs{nullptr, nullptr, nullptr, 0, r, 1}, r, (n + r - 1) / r, stream);
+}
+
+// Landmark part of window + sinks + landmarks every r: the landmarks below
+// the window and not below g (lse of rows without one: -inf, o = 0).
+hipError_t launch_landmark_part(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
+                                int heads, int kv_heads, int n, int d, int w, int g, int r, float scale, bool bf16,
+                                hipStream_t stream) {
+    return launch_prefill_t<kStrided>(q, k, v, o, lse, batch, heads, kv_heads, n, d, w, g, scale, 0.f, bf16,
+                                      PathArgs{nullptr, nullptr, nullptr, 0, r, 2}, 1, n, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -225,6 +225,34 @@ int swa_decode_fwd_fp8(const void *q, const void *k_cache, const void *v_cache,
                        float scale, float sink_bias, swa_dtype_t dtype,
                        void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Fixed sparse patterns on the same block-sparse tiles ("Sliding Window and
+ * Sparse Attention, from Longformer to CSA2", s2 dilated windows, s4
+ * block-sparse attention as a kernel primitive; "Local and Sparse
+ * Attention: Reading Fewer Token Positions", Figure 2).  Shapes, grouping,
+ * dtypes, alignment and errors as swa_prefill_fwd_gqa; r >= 1.
+ *
+ * swa_dilated_prefill_fwd: query i reads the w keys i, i-r, ..., i-(w-1)r
+ * (those >= 0): the cost of a window of w over a span of (w-1)r+1.  No sinks.
+ * r = 1 is the plain window.
+ *
+ * swa_landmark_prefill_fwd: query i reads its window i-w+1 .. i, the sinks
+ * 0 .. g-1 and the landmarks, every position j <= i with j mod r == 0, each
+ * position once; sink_bias on positions < g.  Computed as the window-and-
+ * sinks part into o, the part over the landmarks below the window and not
+ * below g into the workspace, and an LSE merge (swa_lse_merge) into o.
+ * workspace: at least swa_landmark_workspace_bytes(...) bytes, 16-byte
+ * aligned (SWA_EWORKSPACE otherwise).
+ */
+int swa_dilated_prefill_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                            int batch, int heads, int kv_heads, int n, int d, int w, int r,
+                            float scale, swa_dtype_t dtype, hipStream_t stream);
+int swa_landmark_prefill_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                             int batch, int heads, int kv_heads, int n, int d, int w, int g, int r,
+                             float scale, float sink_bias, swa_dtype_t dtype,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+size_t swa_landmark_workspace_bytes(int batch, int heads, int n, int d, swa_dtype_t dtype);
+
 /* Static description of a status code. */
 const char *swa_strerror(int status);
 

@@ -221,3 +221,43 @@ def _decode_fp8(**kw):
 def test_decode_fp8_rejects(kw, want):
     assert _decode_fp8(**kw) == want
 
+
+
+def _dilated(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, batch=1, heads=2, kv_heads=2, n=64, d=128, w=4, r=2, scale=0.125,
+             dtype=1)
+    a.update(kw)
+    return swa.lib().swa_dilated_prefill_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["batch"], a["heads"],
+                                             a["kv_heads"], a["n"], a["d"], a["w"], a["r"], a["scale"], a["dtype"],
+                                             None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), EINVAL), (dict(r=0), EINVAL), (dict(w=0), EINVAL), (dict(n=0), EINVAL),
+    (dict(kv_heads=3), EINVAL), (dict(d=48), EUNSUP), (dict(o=P + 4), EALIGN),
+])
+def test_dilated_rejects(kw, want):
+    assert _dilated(**kw) == want
+
+
+def _landmark(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, batch=1, heads=2, kv_heads=2, n=64, d=128, w=4, g=0, r=2, scale=0.125,
+             bias=0.0, dtype=1, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return swa.lib().swa_landmark_prefill_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["batch"], a["heads"],
+                                              a["kv_heads"], a["n"], a["d"], a["w"], a["g"], a["r"], a["scale"],
+                                              a["bias"], a["dtype"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), EINVAL), (dict(r=0), EINVAL), (dict(g=-1), EINVAL), (dict(bias=float("nan")), EINVAL),
+    (dict(d=48), EUNSUP), (dict(ws=None), EWS), (dict(wsb=100), EWS), (dict(ws=P + 8), EALIGN),
+])
+def test_landmark_rejects(kw, want):
+    assert _landmark(**kw) == want
+
+
+def test_landmark_workspace_size():
+    # o of the landmark part (bf16) plus two fp32 lse rows, each rounded up to 256 bytes
+    assert swa.landmark_workspace_bytes(1, 2, 64, 128, 1) == 1 * 2 * 64 * 128 * 2 + 2 * 512
+    assert swa.landmark_workspace_bytes(1, 2, 64, 96, 1) == 0
