@@ -18,7 +18,8 @@ hipError_t launch_decode(const void *q, const void *kc, const void *vc, const in
                          bool bf16, void *ws, hipStream_t stream);
 hipError_t launch_kv_append(void *kc, void *vc, const void *kn, const void *vn, const int64_t *pos, int batch,
                             int heads, int tn, int d, int w, int g, bool bf16, hipStream_t stream);
-size_t decode_workspace_bytes(int batch, int heads, int kv_heads, int d, int rows, int cap = 8);
+size_t decode_workspace_bytes(int batch, int heads, int kv_heads, int d, int rows, int kind);
+int decode_kind(bool bf16, bool fp8, int heads, int kv_heads);
 hipError_t launch_chunk_prefill(const void *q, const void *k_new, const void *v_new, const void *k_cache,
                                 const void *v_cache, const int64_t *pos, void *o, float *lse, int batch, int heads,
                                 int kv_heads, int t, int d, int w, int g, float scale, float sink_bias, int part,
@@ -255,7 +256,7 @@ int swa_decode_fwd_fp8(const void *q, const void *k_cache, const void *v_cache, 
         (reinterpret_cast<uintptr_t>(pos) & 7u) || (lse && !aligned4(lse)) || !aligned4(k_scale) ||
         !aligned4(v_scale))
         return SWA_EALIGN;
-    const size_t need = swa::decode_workspace_bytes(batch, heads, kv_heads, d, g + w, 4);
+    const size_t need = swa::decode_workspace_bytes(batch, heads, kv_heads, d, g + w, 1);
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return SWA_EWORKSPACE;
         if (!aligned16(workspace)) return SWA_EALIGN;
@@ -269,7 +270,7 @@ size_t swa_decode_workspace_bytes_gqa(int batch, int heads, int kv_heads, int d,
     if (batch < 1 || heads < 1 || w < 1 || g < 0 || (d != 64 && d != 128)) return 0;
     if (kv_heads < 1 || kv_heads > heads || heads % kv_heads != 0) return 0;
     if ((long long)g + w > INT_MAX / 2 || (long long)batch * heads > INT_MAX / 64) return 0;
-    return swa::decode_workspace_bytes(batch, heads, kv_heads, d, g + w);
+    return swa::decode_workspace_bytes(batch, heads, kv_heads, d, g + w, -1);
 }
 
 size_t swa_decode_workspace_bytes(int batch, int heads, int d, int w, int g) {
@@ -291,7 +292,8 @@ int swa_decode_fwd_gqa(const void *q, const void *k_cache, const void *v_cache, 
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
         (reinterpret_cast<uintptr_t>(pos) & 7u) || (lse && !aligned4(lse)))
         return SWA_EALIGN;
-    const size_t need = swa::decode_workspace_bytes(batch, heads, kv_heads, d, g + w);
+    const size_t need = swa::decode_workspace_bytes(batch, heads, kv_heads, d, g + w,
+                                                    swa::decode_kind(dtype == SWA_BF16, false, heads, kv_heads));
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return SWA_EWORKSPACE;
         if (!aligned16(workspace)) return SWA_EALIGN;

@@ -339,6 +339,288 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Grouped-query decode on the matrix cores (bf16 q and cache).  The query
+// heads that share one key/value head are the 16-wide side of
+// v_mfma_f32_16x16x32_bf16 (heads past the group's are zero):
+//   S^T[16 keys x 16 heads] = K[16 keys x 32 d] Q^T    (D/32 MFMAs)
+//   O^T[16 d x 16 heads]   += V^T[16 d x 32 keys] P^T  (one per 16 columns of d)
+// so each cache row is read once for the whole group and the dot products
+// leave the VALU.  K fragments come straight from memory in the A-operand
+// layout (lane l: key l%16, d 8(l/16) .. +8 of a 32-wide step); V goes to
+// LDS by DMA (64-byte column blocks) and is read transposed with
+// ds_read_b64_tr_b16.  Lane l holds head l%16 in S^T, P^T and O^T alike, so a
+// head's softmax state sits in the 4 lanes l%16 = h and the accumulators need
+// no cross-lane traffic; the reference max moves lazily as in the prefill.
+// Each wave takes every 4th block of 32 cache rows of the workgroup's share,
+// one block ahead in flight; waves merge through LDS at the end.
+constexpr int kMfmaRows = 32;  // cache rows per block
+
+// Query heads per MFMA-decode workgroup: the largest divisor of the group
+// size that is at most 16.
+int decode_mfma_heads_per_wg(int group) {
+    for (int h = 16; h > 1; --h)
+        if (group % h == 0) return h;
+    return 1;
+}
+
+typedef float mf32x4 __attribute__((ext_vector_type(4)));
+
+// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt
+// in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+constexpr int vmcnt_only(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
+typedef short ms16x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte buffer load of every lane into LDS at lds + 16 * lane (one wave).
+__device__ __forceinline__ void dma16_lds(__amdgpu_buffer_rsrc_t r, uint8_t *lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ ms16x4 lds_tr16(const uint8_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) ms16x4 *)p);
+}
+
+// lane l <-> lane l^16 exchange combined by max / sum (v_permlane16_swap
+// pairs 16-lane rows 0-1 and 2-3)
+__device__ __forceinline__ float quarter_swap_max(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float quarter_swap_sum(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D>
+__global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
+    const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kcp, const uint16_t *__restrict__ vcp,
+    const int64_t *__restrict__ pos, uint16_t *__restrict__ op, float *__restrict__ lsep, int heads, int kv_heads,
+    int gw, int w, int g, float c2, float scale, float bias_raw, int splits, int rows_per_split,
+    float *__restrict__ ws) {
+    constexpr int KS = D / 32;              // 32-wide d steps of the score product
+    constexpr int DB = D / 16;              // 16-wide column blocks of the output
+    constexpr int kRowBytes = D * 2;
+    constexpr int kBlockBytes = kMfmaRows * kRowBytes;  // one V block in LDS
+    constexpr int kDma = kBlockBytes / 1024;            // 1 KB DMA loads per V block
+    constexpr int kWaves = kDecThreads / 64;
+    // LDS: per wave two V blocks; reused for the cross-wave merge at the end
+    constexpr int kVBytes = kWaves * 2 * kBlockBytes;
+    constexpr int kMergeBytes = kWaves * 16 * (D + 2) * 4;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kVBytes > kMergeBytes ? kVBytes : kMergeBytes];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hl = lane & 15, grp = lane >> 4;
+    const int split = blockIdx.x % splits;
+    const int job = blockIdx.x / splits;
+    const int G = heads / kv_heads;
+    const int chunks = G / gw;
+    const int chunk = job % chunks;
+    const int kvu = job / chunks;  // batch * kv_heads + kv head
+    const int b = kvu / kv_heads;
+    const int h0 = (kvu % kv_heads) * G + chunk * gw;
+    const int unit0 = b * heads + h0;
+    const int R = g + w;
+    const int64_t p = pos[b];
+    const uint16_t *kc = kcp + (size_t)kvu * R * D;
+    const uint16_t *vc = vcp + (size_t)kvu * R * D;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc, (uint32_t)R * kRowBytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc, (uint32_t)R * kRowBytes);
+
+    // Q^T as the B operand: head hl, d 32 ks + 8 grp .. +8 (zero past the group)
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (hl < gw) x = *reinterpret_cast<const uint4 *>(qp + (size_t)(unit0 + hl) * D + 32 * ks + 8 * grp);
+        qf[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+
+    // ring geometry for this query position (as in decode_kernel)
+    const bool ring_full = (p >= (int64_t)w - 1);
+    const int pm = (p >= 0) ? (int)(p % w) : 0;
+    const int64_t win_lo = p - w + 1;
+
+    const int r_begin = split * rows_per_split;
+    const int r_end = min(R, r_begin + rows_per_split);
+    const int nblk = (r_end - r_begin + kMfmaRows - 1) / kMfmaRows;
+
+    // V DMA: load i of a block fills LDS bytes [1 KB i, 1 KB (i+1)): column
+    // block c = byte / (32 * 64), key (byte % 2048) / 64, 16-byte piece.
+    uint32_t voffs[kDma];
+#pragma unroll
+    for (int i = 0; i < kDma; ++i) {
+        const int o = 1024 * i + 16 * lane;
+        const int cblk = o / (kMfmaRows * 64), key = (o % (kMfmaRows * 64)) / 64, piece = (o % 64) / 16;
+        voffs[i] = (uint32_t)key * kRowBytes + cblk * 64 + piece * 16;
+    }
+    uint8_t *vb0 = smem + wave * 2 * kBlockBytes;
+    // transposed V read: lane j of group grp supplies key (row) j/4 of the
+    // group's 4 keys and the 8-byte piece of columns 4 (j%4) .. +3
+    const uint32_t vrd = (uint32_t)((hl >> 2) * 64 + 8 * (hl & 3));
+
+    mf32x4 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = mf32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = kNegInf, negm = 0.f, l_run = 0.f;
+    const float tau = 8.f / c2;
+
+    // K fragments of one block: [16-key half][d step]
+    auto load_k = [&](int blk, bf16x8 (&kx)[2][KS]) {
+        const int row0 = r_begin + blk * kMfmaRows;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                kx[rb][ks] = __builtin_bit_cast(
+                    bf16x8, buffer_load16(rk, (uint32_t)(row0 + 16 * rb + hl) * kRowBytes + (32 * ks + 8 * grp) * 2));
+    };
+    auto load_v = [&](int blk, int buf) {
+        const int row0 = r_begin + blk * kMfmaRows;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(vc + (size_t)row0 * D, (uint32_t)(R - row0) * kRowBytes);
+#pragma unroll
+        for (int i = 0; i < kDma; ++i) dma16_lds(r, vb0 + buf * kBlockBytes + 1024 * i, voffs[i]);
+    };
+    // one block: scores, mask, softmax, O^T += V^T P^T
+    auto compute = [&](int blk, int buf, const bf16x8 (&kx)[2][KS]) {
+        const int row0 = r_begin + blk * kMfmaRows;
+        mf32x4 s[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            s[rb] = mf32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx[rb][ks], qf[ks], s[rb], 0, 0, 0);
+        }
+        // lane (hl, grp) holds keys 16 rb + 4 grp + i of the block: which
+        // position each row holds and whether it is read (as in decode_kernel)
+        float mx = kNegInf;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = row0 + 16 * rb + 4 * grp + i;
+                const int sl = r - g;
+                int dd = pm - sl;
+                dd += (dd < 0) ? w : 0;
+                const int64_t t = (r < g) ? (int64_t)r : (ring_full ? p - dd : (int64_t)sl);
+                const bool v_sink = ((int64_t)r <= p) && ((int64_t)r < win_lo);
+                const bool v_ring = ring_full || ((int64_t)sl <= p);
+                const bool valid = (r < r_end) && (p >= 0) && ((r < g) ? v_sink : v_ring);
+                const float x = s[rb][i] + ((t < g) ? bias_raw : 0.f);
+                s[rb][i] = valid ? x : kNegInf;
+                mx = fmaxf(mx, s[rb][i]);
+            }
+        mx = half_swap_max(quarter_swap_max(mx));  // over the head's 4 lanes
+        if (__any(mx > m_run + tau)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_run - m_new) * c2);
+            m_run = m_new;
+            negm = (m_new == kNegInf) ? 0.f : -m_new * c2;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        }
+        // P^T as the B operand: keys 4 grp + i of half 0, then of half 1
+        bf16x8 pk;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pk[4 * rb + i] = static_cast<__bf16>(fast_exp2(fmaf(s[rb][i], c2, negm)));
+        {
+            const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+            const bf16x2 p01 = {pk[0], pk[1]}, p23 = {pk[2], pk[3]}, p45 = {pk[4], pk[5]}, p67 = {pk[6], pk[7]};
+            float ls = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, 0.f, false);
+            ls = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, ls, false);
+            ls = __builtin_amdgcn_fdot2_f32_bf16(p45, ones, ls, false);
+            l_run += __builtin_amdgcn_fdot2_f32_bf16(p67, ones, ls, false);
+        }
+        const uint8_t *vb = vb0 + buf * kBlockBytes;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const uint8_t *base = vb + (db >> 1) * (kMfmaRows * 64) + 32 * (db & 1) + vrd;
+            const ms16x4 lo = lds_tr16(base + (4 * grp) * 64);
+            const ms16x4 hi = lds_tr16(base + (16 + 4 * grp) * 64);
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pk, oacc[db], 0, 0, 0);
+        }
+    };
+
+    // this wave's blocks wave, wave + 4, ...: two in flight, buffers 0 and 1
+    // alternating (the loop is unrolled by two so that each has fixed registers)
+    const int my_blocks = (nblk > wave) ? (nblk - wave + kWaves - 1) / kWaves : 0;
+    bf16x8 ka[2][KS], kb[2][KS];
+    if (my_blocks > 0) {
+        load_k(wave, ka);
+        load_v(wave, 0);
+    }
+    for (int it = 0; it < my_blocks; it += 2) {
+        const int blk = wave + it * kWaves;
+        if (it + 1 < my_blocks) {
+            load_k(blk + kWaves, kb);
+            load_v(blk + kWaves, 1);
+            __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * KS + kDma));  // block it has landed
+        } else {
+            __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+        }
+        compute(blk, 0, ka);
+        if (it + 1 >= my_blocks) break;
+        if (it + 2 < my_blocks) {
+            load_k(blk + 2 * kWaves, ka);
+            load_v(blk + 2 * kWaves, 0);
+            __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * KS + kDma));  // block it + 1 has landed
+        } else {
+            __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+        }
+        compute(blk + kWaves, 1, kb);
+    }
+
+    // ---- merge the waves: per head h, (m, l, o[D]) of each wave ----
+    const float l_head = half_swap_sum(quarter_swap_sum(l_run));
+    __syncthreads();  // every wave is done with its V blocks
+    float *sm = reinterpret_cast<float *>(smem);  // [wave][head][D + 2]: o[D], m, l
+    {
+        float *rec = sm + (wave * 16 + hl) * (D + 2);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rec[16 * db + 4 * grp + i] = oacc[db][i];
+        if (grp == 0) {
+            rec[D] = m_run;
+            rec[D + 1] = l_head;
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < gw * D; idx += kDecThreads) {
+        const int h = idx / D, c = idx - h * D;
+        float M = kNegInf;
+#pragma unroll
+        for (int wv = 0; wv < kWaves; ++wv) M = fmaxf(M, sm[(wv * 16 + h) * (D + 2) + D]);
+        const float M_use = (M == kNegInf) ? 0.f : M;
+        float L = 0.f, acc = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < kWaves; ++wv) {
+            const float *rec = sm + (wv * 16 + h) * (D + 2);
+            const float f = fast_exp2((rec[D] - M_use) * c2);
+            L += rec[D + 1] * f;
+            acc += rec[c] * f;
+        }
+        const int unit = unit0 + h;
+        if (splits == 1) {
+            const float x = (L > 0.f) ? acc / L : __builtin_nanf("");
+            op[(size_t)unit * D + c] = (uint16_t)f32_to_bf16_bits(x);
+            if (lsep != nullptr && c == 0) lsep[unit] = (L > 0.f) ? M * scale + logf(L) : __builtin_nanf("");
+        } else {
+            float *rec = ws + ((size_t)unit * splits + split) * (2 + D);
+            rec[2 + c] = acc;
+            if (c == 0) {
+                rec[0] = M;
+                rec[1] = L;
+            }
+        }
+    }
+}
+
 // Merge S partial states of one (batch, head) by log-sum-exp.
 template <typename QT, int D>
 __global__ __launch_bounds__(D) void decode_merge_kernel(const float *__restrict__ ws, void *__restrict__ op,
@@ -377,10 +659,14 @@ int decode_heads_per_wg(int group, int cap) {
 template <typename CK>
 constexpr int heads_cap() { return std::is_same<CK, CacheFp8>::value ? 4 : 8; }
 
-// Split count: enough workgroups to cover the chip, at least 256 cache rows each.
-int decode_splits(int jobs, int rows) {
-    if (jobs >= 1024) return 1;
-    int s = (2048 + jobs - 1) / jobs;
+// Split count: enough workgroups to cover the chip, at least 256 cache rows
+// each.  The VALU kernels aim at 2048 workgroups; the MFMA kernel (two
+// workgroups per CU by LDS) at one round of 512, which measured 7 % faster on
+// 64 x 8 key/value heads than four splits.
+int decode_splits(int jobs, int rows, int kind) {
+    const int target = (kind == 2) ? 512 : 2048;
+    if (jobs >= ((kind == 2) ? 512 : 1024)) return 1;
+    int s = (target + jobs - 1) / jobs;
     int max_s = rows / 256;
     if (max_s < 1) max_s = 1;
     if (s > max_s) s = max_s;
@@ -388,15 +674,32 @@ int decode_splits(int jobs, int rows) {
     return s < 1 ? 1 : s;
 }
 
-// jobs = batch * heads / (query heads per workgroup): workgroups before splitting
-static int decode_jobs(int batch, int heads, int kv_heads, int cap) {
-    return batch * (heads / decode_heads_per_wg(heads / kv_heads, cap));
+// Workgroups before splitting: batch * heads / (query heads per
+// workgroup).  kind: 0 the VALU kernel (up to 8 heads per workgroup), 1 the
+// fp8 VALU kernel (up to 4), 2 the MFMA kernel (up to 16; bf16 groups of 2+).
+static int decode_jobs(int batch, int heads, int kv_heads, int kind) {
+    if (kind == 2) return batch * (heads / decode_mfma_heads_per_wg(heads / kv_heads));
+    return batch * (heads / decode_heads_per_wg(heads / kv_heads, kind == 1 ? 4 : 8));
 }
 
-// Workspace of a launch (0 when it does not split); an fp8 launch (cap 4)
-// never needs more than a bf16/fp32 one (cap 8) of the same shape.
-size_t decode_workspace_bytes(int batch, int heads, int kv_heads, int d, int rows, int cap) {
-    int s = decode_splits(decode_jobs(batch, heads, kv_heads, cap), rows);
+// Which kernel a launch uses.
+int decode_kind(bool bf16, bool fp8, int heads, int kv_heads) {
+    if (fp8) return 1;
+    return (bf16 && heads / kv_heads >= 2) ? 2 : 0;
+}
+
+// Workspace of a launch of this kind (0 when it does not split); kind -1:
+// the most any kind needs (fewest workgroups, most splits).
+size_t decode_workspace_bytes(int batch, int heads, int kv_heads, int d, int rows, int kind) {
+    if (kind < 0) {
+        size_t m = 0;
+        for (int k = 0; k < 3; ++k) {
+            const size_t b = decode_workspace_bytes(batch, heads, kv_heads, d, rows, k);
+            if (b > m) m = b;
+        }
+        return m;
+    }
+    int s = decode_splits(decode_jobs(batch, heads, kv_heads, kind), rows, kind);
     if (s == 1) return 0;
     return (size_t)batch * heads * s * (2 + d) * sizeof(float);
 }
@@ -407,8 +710,9 @@ static hipError_t launch_decode_t(const void *q, const void *kc, const void *vc,
                                   float sink_bias, void *ws, const float *ksc, const float *vsc,
                                   hipStream_t stream) {
     const int R = g + w;
-    const int jobs = decode_jobs(batch, heads, kv_heads, heads_cap<CK>());
-    const int splits = decode_splits(jobs, R);
+    const int kind = std::is_same<CK, CacheFp8>::value ? 1 : 0;
+    const int jobs = decode_jobs(batch, heads, kv_heads, kind);
+    const int splits = decode_splits(jobs, R, kind);
     const int rps = (R + splits - 1) / splits;
     const float c2 = (float)((double)scale * kLog2e);
     const float bias_raw = (float)((double)sink_bias / (double)scale);
@@ -441,9 +745,37 @@ static hipError_t launch_decode_d(const void *q, const void *kc, const void *vc,
 #undef SWA_DEC
 }
 
+template <int D>
+static hipError_t launch_decode_mfma(const void *q, const void *kc, const void *vc, const int64_t *pos, void *o,
+                                    float *lse, int batch, int heads, int kv_heads, int w, int g, float scale,
+                                    float sink_bias, void *ws, hipStream_t stream) {
+    const int R = g + w;
+    const int gw = decode_mfma_heads_per_wg(heads / kv_heads);
+    const int jobs = decode_jobs(batch, heads, kv_heads, 2);
+    const int splits = decode_splits(jobs, R, 2);
+    const int rps = (R + splits - 1) / splits;
+    const float c2 = (float)((double)scale * kLog2e);
+    const float bias_raw = (float)((double)sink_bias / (double)scale);
+    hipLaunchKernelGGL((decode_mfma_kernel<D>), dim3(jobs * splits), dim3(kDecThreads), 0, stream,
+                       (const uint16_t *)q, (const uint16_t *)kc, (const uint16_t *)vc, pos, (uint16_t *)o, lse, heads,
+                       kv_heads, gw, w, g, c2, scale, bias_raw, splits, rps, (float *)ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits == 1) return e;
+    hipLaunchKernelGGL((decode_merge_kernel<uint16_t, D>), dim3(batch * heads), dim3(D), 0, stream,
+                       (const float *)ws, o, lse, splits, c2, scale);
+    return hipGetLastError();
+}
+
 hipError_t launch_decode(const void *q, const void *kc, const void *vc, const int64_t *pos, void *o, float *lse,
                          int batch, int heads, int kv_heads, int d, int w, int g, float scale, float sink_bias,
                          bool bf16, void *ws, hipStream_t stream) {
+    if (decode_kind(bf16, false, heads, kv_heads) == 2) {
+        if (d == 128)
+            return launch_decode_mfma<128>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale, sink_bias,
+                                           ws, stream);
+        return launch_decode_mfma<64>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g, scale, sink_bias, ws,
+                                      stream);
+    }
     if (bf16) {
         if (d == 128)
             return launch_decode_d<uint16_t, CacheBf16, 128>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g,
