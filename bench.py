@@ -72,11 +72,13 @@ PATTERN = {
 # the source has changed since, the figure no longer describes the kernel and
 # `traffic` is reported as null.
 MEASURED_TRAFFIC = {
-    "mistral_prefill": {"bytes": 1810752641, "source_digest": "aab673279bab0e3e"},
-    "sink_prefill": {"bytes": 5454442202, "source_digest": "aab673279bab0e3e"},
-    "gemma3_local_prefill": {"bytes": 4380782777, "source_digest": "aab673279bab0e3e"},
-    "rolling_decode": {"bytes": 4300235981, "source_digest": "d58ef838d6a89d2b"},
-    "gqa_decode": {"bytes": 1081519983, "source_digest": "d58ef838d6a89d2b"},
+    "mistral_prefill": {"bytes": 1779907168, "source_digest": "ff496cdae290da36"},
+    "sink_prefill": {"bytes": 5244102632, "source_digest": "ff496cdae290da36"},
+    "gemma3_local_prefill": {"bytes": 4603199619, "source_digest": "ff496cdae290da36"},
+    "chunk_prefill": {"bytes": 134518393, "source_digest": "ff496cdae290da36"},
+    "rolling_decode": {"bytes": 4300268055, "source_digest": "e3acdbc3d2ecbad9"},
+    "gqa_decode": {"bytes": 1076030201, "source_digest": "e3acdbc3d2ecbad9"},
+    "fp8_decode": {"bytes": 2151020382, "source_digest": "e3acdbc3d2ecbad9"},
 }
 CSRC = os.path.join(ROOT, "block_sparse_causal_band_amd", "csrc")
 
@@ -371,7 +373,8 @@ def bench_decode(name, steps, warmup):
                    "positions": [lo, hi], "kv_bytes_per_step": nbytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel": "decode_kernel<bf16,fp8,128>" if fp8 else "decode_kernel<bf16,bf16,128>",
+                     "kernel": ("decode_kernel<bf16,fp8,128>" if fp8 else
+                                "decode_mfma_kernel<128>" if Hkv < H else "decode_kernel<bf16,bf16,128>"),
                      "avg_launch_ms": ms_launch, "min_launch_ms": min(per)},
     }
 
