@@ -228,7 +228,13 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     constexpr bool CHUNK = (KIND == kChunk), STRIDED = (KIND == kStrided);
     using L = Bf16Tile<D, WAVES>;
     constexpr int BQ = 32 * WAVES;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * L::kStageBytes];
+    // two K and two V tile buffers, as four arrays: the compiler can then see
+    // that the LDS reads of one buffer do not alias the DMA into another and
+    // does not wait for that DMA before them
+    __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[L::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[L::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[L::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t vbuf1[L::kTileBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -334,8 +340,6 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
         dma_k[i] = key * skv * L::kRowBytes + 16 * ck;
         dma_v[i] = key * skv * L::kRowBytes + 16 * cv;
     }
-    uint8_t *const kbuf = smem;                       // K buffers 0, 1
-    uint8_t *const vbuf = smem + 2 * L::kTileBytes;   // V buffers 0, 1
     auto dma_rows = [&](const uint16_t *src, const uint32_t *offs, int r0, int nrows, uint8_t *dst) {
         // rows r0 .. of src, rows >= nrows read as zero
         const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)r0 * D, (uint32_t)(nrows - r0) * L::kRowBytes);
@@ -411,24 +415,29 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     // computes the scores of tile t+1.  During tile t the DMA fills K(t+2) into
     // the K buffer that K(t) left and V(t+1) into the V buffer that V(t-1)
     // left, so every DMA has a whole tile of time to land.
-    dma(true, band.block(0) * kBK, kbuf);
-    dma(false, band.block(0) * kBK, vbuf);
-    if (ntiles > 1) dma(true, band.block(1) * kBK, kbuf + L::kTileBytes);
+    dma(true, band.block(0) * kBK, kbuf0);
+    dma(false, band.block(0) * kBK, vbuf0);
+    if (ntiles > 1) dma(true, band.block(1) * kBK, kbuf1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     f32x16 s_cur[2];
-    scores(kbuf, s_cur);
+    scores(kbuf0, s_cur);
     __syncthreads();  // every wave is done with K(0) before K(2) replaces it
 
-    auto do_tile = [&](int t, auto masked_tag) {
+    auto do_tile_p = [&](int t, auto masked_tag, auto par_tag) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_tag)::value;
-        const int cur = t & 1, nxt = cur ^ 1;
+        constexpr int PAR = decltype(par_tag)::value;  // t & 1, or 2: from t at run time
+        const int par = (PAR == 2) ? (t & 1) : PAR;
+        uint8_t *const kcur = par ? kbuf1 : kbuf0;
+        uint8_t *const knxt = par ? kbuf0 : kbuf1;
+        uint8_t *const vcur = par ? vbuf1 : vbuf0;
+        uint8_t *const vnxt = par ? vbuf0 : vbuf1;
         const int k0 = band.block(t) * kBK;
-        if (t + 2 < ntiles) dma(true, band.block(t + 2) * kBK, kbuf + cur * L::kTileBytes);
-        if (t + 1 < ntiles) dma(false, band.block(t + 1) * kBK, vbuf + nxt * L::kTileBytes);
+        if (t + 2 < ntiles) dma(true, band.block(t + 2) * kBK, kcur);
+        if (t + 1 < ntiles) dma(false, band.block(t + 1) * kBK, vnxt);
 
-        const uint8_t *kb = kbuf + nxt * L::kTileBytes;
-        const uint8_t *vb = vbuf + cur * L::kTileBytes + voff;
+        const uint8_t *kb = knxt;
+        const uint8_t *vb = vcur + voff;
         constexpr int NC = D / 16;       // MFMAs per 32-key score sub-block
         constexpr int NS = 2 * NC;       // score MFMAs per tile
         constexpr int EPS = 32 / NS;     // exponentials per score MFMA
@@ -526,10 +535,27 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     int t_lo = 0, t_hi = ntiles;  // a wave entirely past n keeps all tiles unmasked (nothing is stored)
     const int qw0 = q0 + wave * 32;
     if (qw0 < nq) full_range(band, qpos(qw0), qpos(min(qw0 + 31, nq - 1)), khi, wq, g, kBK, &t_lo, &t_hi, klo);
+    // The FULL run is unrolled by two so that each tile body names its
+    // buffers statically (parity 0 / 1); the cut tiles take the parity at run
+    // time (2).
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using P2 = std::integral_constant<int, 2>;
     int t = 0;
-    for (; t < t_lo; ++t) do_tile(t, std::true_type{});
-    for (; t < t_hi; ++t) do_tile(t, std::false_type{});
-    for (; t < ntiles; ++t) do_tile(t, std::true_type{});
+    for (; t < t_lo; ++t) do_tile_p(t, std::true_type{}, P2{});
+    if ((t & 1) && t < t_hi) {
+        do_tile_p(t, std::false_type{}, P1{});
+        ++t;
+    }
+    for (; t + 1 < t_hi; t += 2) {
+        do_tile_p(t, std::false_type{}, P0{});
+        do_tile_p(t + 1, std::false_type{}, P1{});
+    }
+    if (t < t_hi) {
+        do_tile_p(t, std::false_type{}, P0{});
+        ++t;
+    }
+    for (; t < ntiles; ++t) do_tile_p(t, std::true_type{}, P2{});
 
     store_rows<uint16_t, D>(oacc, m_run, l_run, qi, nq, lh, op + base + (size_t)oq * D,
                             lsep ? lsep + (size_t)unit * n + oq : nullptr, scale, sq);
