@@ -72,10 +72,10 @@ PATTERN = {
 # the source has changed since, the figure no longer describes the kernel and
 # `traffic` is reported as null.
 MEASURED_TRAFFIC = {
-    "mistral_prefill": {"bytes": 1779907168, "source_digest": "ff496cdae290da36"},
-    "sink_prefill": {"bytes": 5244102632, "source_digest": "ff496cdae290da36"},
-    "gemma3_local_prefill": {"bytes": 4603199619, "source_digest": "ff496cdae290da36"},
-    "chunk_prefill": {"bytes": 134518393, "source_digest": "ff496cdae290da36"},
+    "mistral_prefill": {"bytes": 1956739689, "source_digest": "2327d11a2400de92"},
+    "sink_prefill": {"bytes": 5589761303, "source_digest": "2327d11a2400de92"},
+    "gemma3_local_prefill": {"bytes": 4178587146, "source_digest": "2327d11a2400de92"},
+    "chunk_prefill": {"bytes": 134557049, "source_digest": "2327d11a2400de92"},
     "rolling_decode": {"bytes": 4300268055, "source_digest": "e3acdbc3d2ecbad9"},
     "gqa_decode": {"bytes": 1076030201, "source_digest": "e3acdbc3d2ecbad9"},
     "fp8_decode": {"bytes": 2151020382, "source_digest": "e3acdbc3d2ecbad9"},
