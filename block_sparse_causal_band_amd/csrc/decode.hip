@@ -495,6 +495,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
         // lane (hl, grp) holds keys 16 rb + 4 grp + i of the block: which
         // position each row holds and whether it is read (as in decode_kernel)
         float mx = kNegInf;
+        uint32_t vkeep[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};  // per 2 key slots
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -510,7 +511,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
                 const float x = s[rb][i] + ((t < g) ? bias_raw : 0.f);
                 s[rb][i] = valid ? x : kNegInf;
                 mx = fmaxf(mx, s[rb][i]);
+                const int e = 4 * rb + i;  // key slot of this row in the P and V^T operands
+                if (!valid) vkeep[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
             }
+        // a row that is not read may hold anything (an unwritten slot): its
+        // P is 0 and, where such rows occur, its V values are zeroed too, so
+        // that 0 * NaN cannot reach the output
+        const bool any_unread = __any((vkeep[0] & vkeep[1] & vkeep[2] & vkeep[3]) != 0xffffffffu);
         mx = half_swap_max(quarter_swap_max(mx));  // over the head's 4 lanes
         if (__any(mx > m_run + tau)) {
             const float m_new = fmaxf(m_run, mx);
@@ -541,7 +548,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
             const uint8_t *base = vb + (db >> 1) * (kMfmaRows * 64) + 32 * (db & 1) + vrd;
             const ms16x4 lo = lds_tr16(base + (4 * grp) * 64);
             const ms16x4 hi = lds_tr16(base + (16 + 4 * grp) * 64);
-            const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            if (any_unread) {
+                u32x4 u = __builtin_bit_cast(u32x4, vf);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) u[j] &= vkeep[j];
+                vf = __builtin_bit_cast(bf16x8, u);
+            }
             oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pk, oacc[db], 0, 0, 0);
         }
     };

@@ -154,3 +154,12 @@ def test_fp8_decode_full_size_sampled(orc):
     rng = np.random.default_rng(91)
     units = sorted({(int(b), int(h)) for b, h in zip(rng.integers(0, B, 48), rng.integers(0, H, 48))})
     _decode_fp8_vs_oracle(orc, q, kc, vc, ks, vs, pos, w, g, 0.0, units=units)
+
+
+def test_fp8_decode_negative_position_gives_nan():
+    dev = _dev()
+    q, kc, vc, ks, vs, _ = synth.fp8_decode_problem(2, 4, 2, 128, 20, 0, 0, torch.bfloat16, seed=92, device=dev)
+    pos = torch.tensor([-5, 40], dtype=torch.int64, device=dev)
+    o = swa.decode_fp8(q, kc, vc, ks, vs, pos, w=16, g=4)
+    torch.cuda.synchronize()
+    assert torch.isnan(o[0].float()).all() and torch.isfinite(o[1].float()).all()

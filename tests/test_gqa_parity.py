@@ -149,3 +149,37 @@ def test_gqa_rejects_bad_kv_heads():
     k = torch.zeros(1, 4, 64, 64, dtype=torch.bfloat16, device=dev)
     with pytest.raises(Exception):
         swa.prefill(q, k, k, w=8, g=0)
+
+
+def test_decode_gqa_negative_position_and_determinism():
+    """The matrix-core decode: a negative position gives NaN rows, other rows
+    stay finite, and two launches agree bit for bit."""
+    dev = _dev()
+    q, kc, vc, _ = synth.decode_problem(2, 8, 128, 520, 0, 0, torch.bfloat16, seed=68, device=dev, kv_heads=2)
+    pos = torch.tensor([-1, 700], dtype=torch.int64, device=dev)
+    a = swa.decode(q, kc, vc, pos, w=516, g=4)
+    b = swa.decode(q, kc, vc, pos, w=516, g=4)
+    torch.cuda.synchronize()
+    assert torch.isnan(a[0].float()).all() and torch.isfinite(a[1].float()).all()
+    assert torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_decode_gqa_ignores_unwritten_rows(orc, dtype):
+    """NaN in never-written ring slots and sink rows does not reach grouped
+    decode outputs at early positions."""
+    dev = _dev()
+    w, g, d, H, Hkv = 64, 4, 128, 8, 2
+    positions = [0, 1, 5, 30, 62]
+    B, n = len(positions), max(positions) + 1
+    kseq = synth.normal((B, Hkv, n, d), seed=69, dtype=dtype, device="cpu")
+    vseq = synth.normal((B, Hkv, n, d), seed=70, dtype=dtype, device="cpu")
+    q = synth.normal((B, H, d), seed=71, dtype=dtype, device="cpu").to(dev)
+    kc = torch.full((B, Hkv, g + w, d), float("nan"), dtype=dtype, device=dev)
+    vc = torch.full_like(kc, float("nan"))
+    zero = torch.zeros(1, dtype=torch.int64, device=dev)
+    for b, p in enumerate(positions):
+        swa.kv_append(kc[b:b + 1], vc[b:b + 1], kseq[b:b + 1, :, :p + 1].contiguous().to(dev),
+                      vseq[b:b + 1, :, :p + 1].contiguous().to(dev), zero, w=w, g=g)
+    pos = torch.tensor(positions, dtype=torch.int64, device=dev)
+    _decode_gqa_vs_oracle(orc, q, kc, vc, pos, w, g, 0.0)
