@@ -87,6 +87,8 @@ int swa_prefill_fwd_gqa(const void *q, const void *k, const void *v, void *o, fl
     const long long units = (long long)batch * heads;
     const long long nqb = (n + bq - 1) / bq;
     if (units * nqb > INT_MAX) return SWA_EINVAL;
+    // byte offsets within one (batch, head)'s rows stay below 2^32 for the buffer loads
+    if ((long long)n * d * (dtype == SWA_BF16 ? 2 : 4) >= (1LL << 32)) return SWA_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned4(lse)))
         return SWA_EALIGN;
     return status_of(swa::launch_prefill(q, k, v, o, lse, batch, heads, kv_heads, n, d, w, g, scale, sink_bias,
@@ -249,6 +251,7 @@ int swa_decode_fwd_fp8(const void *q, const void *k_cache, const void *v_cache, 
     if (kv_heads < 1 || kv_heads > heads || heads % kv_heads != 0) return SWA_EINVAL;
     if ((long long)g + w > INT_MAX / 2) return SWA_EINVAL;
     if ((long long)batch * heads > INT_MAX / 64) return SWA_EINVAL;
+    if (((long long)g + w) * d * 4 >= (1LL << 32)) return SWA_EINVAL;  // cache bytes of one head, buffer offsets
     if (!std::isfinite(scale) || !(scale > 0.f) || !std::isfinite(sink_bias)) return SWA_EINVAL;
     int st = check_dtype_d(dtype, d);
     if (st != SWA_OK) return st;
@@ -286,6 +289,7 @@ int swa_decode_fwd_gqa(const void *q, const void *k_cache, const void *v_cache, 
     if (kv_heads < 1 || kv_heads > heads || heads % kv_heads != 0) return SWA_EINVAL;
     if ((long long)g + w > INT_MAX / 2) return SWA_EINVAL;
     if ((long long)batch * heads > INT_MAX / 64) return SWA_EINVAL;
+    if (((long long)g + w) * d * 4 >= (1LL << 32)) return SWA_EINVAL;  // cache bytes of one head, buffer offsets
     if (!std::isfinite(scale) || !(scale > 0.f) || !std::isfinite(sink_bias)) return SWA_EINVAL;
     int st = check_dtype_d(dtype, d);
     if (st != SWA_OK) return st;

@@ -72,7 +72,8 @@ enum {
  *   scale      : finite, > 0 (1/sqrt(d) is the usual value)
  *   sink_bias  : finite
  *   n >= 1, w >= 1, g >= 0 (g may exceed n), batch >= 1, heads >= 1,
- *   batch * heads * n * d < 2^31.
+ *   n * d * element size < 2^32 (one (batch, head)'s rows are addressed
+ *   with 32-bit byte offsets; SWA_EINVAL otherwise).
  * Only the key tiles that hold attended pairs are visited (the diagonal band
  * plus the sink tiles below it); nothing n x n is ever formed.  K and V rows
  * at positions >= n are never read.
@@ -107,6 +108,7 @@ int swa_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v
  *   pos       : [batch] int64, device, >= 0 (a negative entry yields NaN output)
  *   workspace : device scratch of at least swa_decode_workspace_bytes(...)
  *               bytes, 16-byte aligned, or NULL when that size is 0.
+ *   (g + w) * d * 4 < 2^32 (one head's cache rows, 32-bit byte offsets).
  * Ring slot s is read only when it holds a position of the window; sink row t
  * is read only when position t has left the window (otherwise the ring copy
  * is the one read, so each position is read once).

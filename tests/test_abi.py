@@ -261,3 +261,11 @@ def test_landmark_workspace_size():
     # o of the landmark part (bf16) plus two fp32 lse rows, each rounded up to 256 bytes
     assert swa.landmark_workspace_bytes(1, 2, 64, 128, 1) == 1 * 2 * 64 * 128 * 2 + 2 * 512
     assert swa.landmark_workspace_bytes(1, 2, 64, 96, 1) == 0
+
+
+def test_row_byte_limits():
+    # one (batch, head)'s rows are addressed with 32-bit byte offsets
+    assert _prefill(n=(1 << 24), d=128, dtype=1) == EINVAL            # 2^24 rows x 256 B = 2^32
+    assert _prefill(n=(1 << 23), d=128, dtype=0) == EINVAL            # fp32: 2^23 x 512 B
+    assert _decode(w=(1 << 23), g=0, d=128) == EINVAL                  # cache rows x d x 4 >= 2^32
+    assert _decode_fp8(w=(1 << 23), g=0, d=128) == EINVAL
