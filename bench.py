@@ -76,9 +76,9 @@ MEASURED_TRAFFIC = {
     "sink_prefill": {"bytes": 5589761303, "source_digest": "2327d11a2400de92"},
     "gemma3_local_prefill": {"bytes": 4178587146, "source_digest": "2327d11a2400de92"},
     "chunk_prefill": {"bytes": 134557049, "source_digest": "2327d11a2400de92"},
-    "rolling_decode": {"bytes": 4300268055, "source_digest": "e3acdbc3d2ecbad9"},
-    "gqa_decode": {"bytes": 1076030201, "source_digest": "e3acdbc3d2ecbad9"},
-    "fp8_decode": {"bytes": 2151020382, "source_digest": "e3acdbc3d2ecbad9"},
+    "rolling_decode": {"bytes": 4300264727, "source_digest": "527a4c305b64a28c"},
+    "gqa_decode": {"bytes": 1076055801, "source_digest": "527a4c305b64a28c"},
+    "fp8_decode": {"bytes": 2151022590, "source_digest": "527a4c305b64a28c"},
 }
 CSRC = os.path.join(ROOT, "block_sparse_causal_band_amd", "csrc")
 
