@@ -29,7 +29,11 @@
 //    FMA per score.  The reference max only moves when a score exceeds it by
 //    more than 2^8 in probability, so the O rescale is rare.  A row with no
 //    attended key yet keeps m = -inf and is guarded so that no -inf - -inf is
-//    ever formed.
+//    ever formed.  FULL tiles do not even take the row max first: their
+//    probabilities are formed against the current reference, and only when
+//    some lane's bf16 sum of them reaches 2^7 (a superset of the cases that
+//    move the reference) is the exact update run and the tile's
+//    probabilities formed again, so the result is the same bit for bit.
 //
 // bf16 path: K and V tiles go HBM -> LDS by buffer loads that write LDS
 // directly (16 bytes per lane, out-of-range rows come back as zeros), so no
@@ -456,25 +460,26 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
             const s16x4 hi = lds_read_tr16(p0 + 8 * 64);
             return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         };
-        // Every K fragment of tile t+1 is read before the mask and the row
-        // max of tile t, whose VALU work then covers the LDS latency.
+        // Every K fragment of tile t+1 is read at the top of the tile (on cut
+        // tiles the mask and the row max of tile t then cover the latency).
         bf16x8 kf[NS];
 #pragma unroll
         for (int j = 0; j < NS; ++j) kf[j] = kfrag(j);
 
-        if constexpr (MASKED) mask_tile<CHUNK || STRIDED>(s_cur, qa, k0, lh, khi, wq, g, bias_raw, klo);
-        update_max(s_cur, m_run, negm, l_run, oacc, c2, tau);
+        if constexpr (MASKED) {
+            mask_tile<CHUNK || STRIDED>(s_cur, qa, k0, lh, khi, wq, g, bias_raw, klo);
+            update_max(s_cur, m_run, negm, l_run, oacc, c2, tau);
+        }
 
         // The rest of the tile is two interleaved streams, in a fixed order
         // (sched_barrier pins it; the compiler would otherwise group like
         // with like, and long runs of MFMAs with no VALU work between them
         // leave the matrix core and the VALU taking turns):
         //  A: the score MFMAs of tile t+1, each followed by the exponentials
-        //     of 32/NS scores of tile t; the first V^T fragments of B are
-        //     read during its last MFMAs;
-        //  B: the PV MFMAs of tile t, each group of them preceded by the
-        //     bf16 packing and row-sum dot2s of its probabilities (V^T
-        //     fragments read 3 MFMAs ahead).
+        //     of 32/NS scores of tile t, their bf16 packing and row-sum
+        //     dot2s; the first V^T fragments of B are read during its last
+        //     MFMAs;
+        //  B: the PV MFMAs of tile t (V^T fragments read 3 MFMAs ahead).
         // On the last tile the A stream reads the other K buffer and its
         // result is discarded.  The whole stretch runs at raised wave
         // priority, so when both waves of a SIMD are ready the one feeding
@@ -486,32 +491,48 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) s_nxt[sb][r] = 0.f;
         bf16x8 vf[VA];
+        const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+        // probabilities of tile t as bf16 pairs: word i holds flat scores 2i, 2i+1
+        // (flat e = 16 sb + r); the row-sum dot2s alternate between two sums
+        uint32_t pw[16];
+        float ls0 = 0.f, ls1 = 0.f;
+        auto prob_pair = [&](int i) __attribute__((always_inline)) {
+            const int e = 2 * i;
+            const float a = fast_exp2(fmaf(s_cur[e >> 4][e & 15], c2, negm));
+            const float b = fast_exp2(fmaf(s_cur[(e + 1) >> 4][(e + 1) & 15], c2, negm));
+            const bf16x2 pr = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+            pw[i] = __builtin_bit_cast(uint32_t, pr);
+            if (i & 1) ls1 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls1, false);
+            else ls0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls0, false);
+        };
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
             if (j >= NS - VA) vf[j - (NS - VA)] = vfrag(j - (NS - VA));
             s_nxt[j / NC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j], qf[j % NC], s_nxt[j / NC], 0, 0, 0);
 #pragma unroll
-            for (int q = 0; q < EPS; ++q) {
-                const int e = EPS * j + q;
-                s_cur[e >> 4][e & 15] = fast_exp2(fmaf(s_cur[e >> 4][e & 15], c2, negm));
-            }
+            for (int q = 0; q < EPS / 2; ++q) prob_pair((EPS / 2) * j + q);
             __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (!MASKED) {
+            // The reference max moves only if some probability reached 2^8;
+            // a lane whose bf16 row sum stays below 2^7 has none, so the
+            // exact update (and a recomputation) runs only when a lane's sum
+            // reaches 2^7, or the row has no reference yet.
+            const float lsum = ls0 + ls1;
+            if (__any(!(lsum < 128.f) || m_run == kNegInf)) {
+                update_max(s_cur, m_run, negm, l_run, oacc, c2, tau);
+                ls0 = 0.f;
+                ls1 = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) prob_pair(i);
+            }
+        }
 
-        const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
-        float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
             // probabilities of keys 16 kc + {4 lh + 0..3, 8 + 4 lh + 0..3}, rounded to bf16
-            bf16x8 pk;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pk[e] = static_cast<__bf16>(s_cur[kc >> 1][8 * (kc & 1) + e]);
-            const bf16x2 p01 = {pk[0], pk[1]}, p23 = {pk[2], pk[3]};
-            const bf16x2 p45 = {pk[4], pk[5]}, p67 = {pk[6], pk[7]};
-            ls0 = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, ls0, false);
-            ls1 = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, ls1, false);
-            ls0 = __builtin_amdgcn_fdot2_f32_bf16(p45, ones, ls0, false);
-            ls1 = __builtin_amdgcn_fdot2_f32_bf16(p67, ones, ls1, false);
+            const bf16x8 pk =
+                __builtin_bit_cast(bf16x8, make_uint4(pw[4 * kc], pw[4 * kc + 1], pw[4 * kc + 2], pw[4 * kc + 3]));
 #pragma unroll
             for (int cb = 0; cb < D / 32; ++cb) {
                 const int j = kc * (D / 32) + cb;

@@ -157,6 +157,26 @@ def test_never_reads_past_n(orc):
     assert float(np.max(np.abs(o[0, 0].float().cpu().numpy() - ro))) <= BF16_TOL
 
 
+@pytest.mark.parametrize("case", ["ramp", "spikes"])
+def test_reference_max_moves_inside_full_tiles(orc, case):
+    """Scores that keep rising along the sequence (keys scaled up with their
+    position), or single keys whose scores jump far past everything before
+    them (some past the fp32 range of 2^x against the old reference), make the
+    running reference max move inside runs of FULL tiles, where the kernel
+    forms the probabilities before it knows the tile's row max."""
+    dev = _dev()
+    B, H, n, d, w, g = 1, 2, 1500, 128, 300, 2
+    q, k, v = synth.qkv(B, H, n, d, torch.bfloat16, seed=31, device="cpu")
+    if case == "ramp":
+        k = (k.float() * torch.linspace(0.3, 3.0, n).view(1, 1, n, 1)).to(torch.bfloat16)
+    else:
+        kf = k.float()
+        for j, a in ((400, 12.0), (700, 40.0), (701, -40.0), (1000, 80.0), (1333, 25.0)):
+            kf[:, :, j] *= a
+        k = kf.to(torch.bfloat16)
+    _compare(orc, q.to(dev), k.to(dev), v.to(dev), w, g, 1.0)
+
+
 def test_deterministic():
     dev = _dev()
     q, k, v = synth.qkv(1, 4, 3000, 128, torch.bfloat16, seed=21, device=dev)
