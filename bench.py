@@ -72,10 +72,10 @@ PATTERN = {
 # the source has changed since, the figure no longer describes the kernel and
 # `traffic` is reported as null.
 MEASURED_TRAFFIC = {
-    "mistral_prefill": {"bytes": 1956739689, "source_digest": "2327d11a2400de92"},
-    "sink_prefill": {"bytes": 5589761303, "source_digest": "2327d11a2400de92"},
-    "gemma3_local_prefill": {"bytes": 4178587146, "source_digest": "2327d11a2400de92"},
-    "chunk_prefill": {"bytes": 134557049, "source_digest": "2327d11a2400de92"},
+    "mistral_prefill": {"bytes": 1852309432, "source_digest": "a80e44a6a9735a84"},
+    "sink_prefill": {"bytes": 5067995080, "source_digest": "a80e44a6a9735a84"},
+    "gemma3_local_prefill": {"bytes": 3943029004, "source_digest": "a80e44a6a9735a84"},
+    "chunk_prefill": {"bytes": 138366917, "source_digest": "a80e44a6a9735a84"},
     "rolling_decode": {"bytes": 4300264727, "source_digest": "527a4c305b64a28c"},
     "gqa_decode": {"bytes": 1076055801, "source_digest": "527a4c305b64a28c"},
     "fp8_decode": {"bytes": 2151022590, "source_digest": "527a4c305b64a28c"},
