@@ -62,8 +62,10 @@ constexpr int kXcds = 8;
 // Workgroup id -> (unit = batch*head, query block).  Ids that land on the same
 // XCD (id % 8) get a contiguous run of logical work, so neighbouring query
 // blocks of one head -- which read overlapping K/V windows -- share that XCD's
-// L2.  Within a head the query blocks run from the last to the first, so the
-// short ramp blocks at the start of the sequence are the last ones dispatched.
+// L2.  Within a head the query blocks run from the first to the last, so a
+// block's first key tiles (the low end of its window) are the ones the block
+// before it has just read into that L2, and the tiles no earlier block
+// touched (the diagonal) come last, after the block is under way.
 __host__ __device__ inline void workgroup_order(int bid, int total, int nqb, int *unit, int *qb) {
     int xcd = bid % kXcds;
     int slot = bid / kXcds;
@@ -71,7 +73,7 @@ __host__ __device__ inline void workgroup_order(int bid, int total, int nqb, int
     int rem = total % kXcds;
     int logical = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
     *unit = logical / nqb;
-    *qb = nqb - 1 - (logical % nqb);
+    *qb = logical % nqb;
 }
 
 // The FULL tiles of query rows [qa, qz] (qz < n) are one contiguous run

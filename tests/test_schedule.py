@@ -90,3 +90,14 @@ def test_workgroup_order_keeps_heads_on_one_xcd():
     for xcd in range(8):
         units = order[xcd::8, 0]
         assert len(np.unique(units)) == 4  # 32 heads x 128 blocks over 8 XCDs
+
+
+def test_workgroup_order_runs_blocks_first_to_last():
+    """Within each XCD's run a head's query blocks come in increasing order, so
+    the low end of a block's window is what the block before it just read."""
+    order = swa.prefill_order(32, 128)
+    for xcd in range(8):
+        run = order[xcd::8]
+        for u in np.unique(run[:, 0]):
+            qbs = run[run[:, 0] == u, 1]
+            assert np.all(np.diff(qbs) == 1) and qbs[0] == 0
