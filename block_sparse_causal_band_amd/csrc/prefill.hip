@@ -201,6 +201,43 @@ __device__ __forceinline__ void store_rows(const f32x16 (&oacc)[D / 32], float m
     if (lse != nullptr && lh == 0) lse[(size_t)qi * rs] = m_run * scale + logf(l_tot);
 }
 
+
+// bf16 output of one wave through LDS: the wave's 32 rows are written into
+// its own 32 * 2D-byte region (16-byte chunk k of row r at chunk position
+// k ^ (r % (2D/16)), so that the 32 rows of one column do not share banks),
+// then read back row by row, 16 bytes per lane, and stored as whole rows
+// (2D/16 lanes per row).  The region is LDS no other wave touches; a wave's
+// own LDS writes and reads are ordered.
+template <int D>
+__device__ __forceinline__ void store_rows_lds(const f32x16 (&oacc)[D / 32], float m_run, float l_run, int qw0, int nq,
+                                               int lr, int lh, int lane, uint16_t *O, float *lse, float scale,
+                                               int rs, uint8_t *region) {
+    constexpr int RB = 2 * D;      // bytes per row
+    constexpr int CPR = RB / 16;   // 16-byte chunks per row
+    const float l_tot = half_swap_sum(l_run);
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            // columns 32 cb + 8 gq + 4 lh .. +3: chunk 4 cb + gq, byte 8 lh in it
+            const int ch = 4 * cb + gq;
+            const float x0 = oacc[cb][4 * gq + 0] * inv, x1 = oacc[cb][4 * gq + 1] * inv;
+            const float x2 = oacc[cb][4 * gq + 2] * inv, x3 = oacc[cb][4 * gq + 3] * inv;
+            *reinterpret_cast<uint2 *>(region + lr * RB + ((ch ^ (lr % CPR)) * 16) + 8 * lh) =
+                make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
+        }
+#pragma unroll
+    for (int j = 0; j < 32 * CPR / 64; ++j) {
+        const int idx = 64 * j + lane;
+        const int r = idx / CPR, ch = idx % CPR;
+        const uint4 v = *reinterpret_cast<const uint4 *>(region + r * RB + ((ch ^ (r % CPR)) * 16));
+        if (qw0 + r < nq) *reinterpret_cast<uint4 *>(O + (size_t)(qw0 + r) * rs * D + 8 * ch) = v;
+    }
+    const int qi = qw0 + lr;
+    if (lse != nullptr && lh == 0 && qi < nq) lse[(size_t)qi * rs] = m_run * scale + logf(l_tot);
+}
+
 // ---------------------------------------------------------------------------
 // bf16 path.
 template <int D, int WAVES>
@@ -578,8 +615,12 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     }
     for (; t < ntiles; ++t) do_tile_p(t, std::true_type{}, P2{});
 
-    store_rows<uint16_t, D>(oacc, m_run, l_run, qi, nq, lh, op + base + (size_t)oq * D,
-                            lsep ? lsep + (size_t)unit * n + oq : nullptr, scale, sq);
+    // the loop's last barrier has every wave past its LDS reads; each wave
+    // stages its rows in its own 32 * 2D bytes of the K buffers
+    static_assert(2 * 32 * 2 * D <= L::kTileBytes, "two waves' rows per K buffer");
+    uint8_t *const region = ((wave < 2) ? kbuf0 : kbuf1) + (wave & 1) * (32 * 2 * D);
+    store_rows_lds<D>(oacc, m_run, l_run, q0 + wave * 32, nq, lr, lh, lane, op + base + (size_t)oq * D,
+                      lsep ? lsep + (size_t)unit * n + oq : nullptr, scale, sq, region);
 }
 
 // ---------------------------------------------------------------------------
