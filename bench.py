@@ -72,10 +72,10 @@ PATTERN = {
 # the source has changed since, the figure no longer describes the kernel and
 # `traffic` is reported as null.
 MEASURED_TRAFFIC = {
-    "mistral_prefill": {"bytes": 538035556, "source_digest": "855fe08802303e60"},
-    "sink_prefill": {"bytes": 1074759383, "source_digest": "855fe08802303e60"},
-    "gemma3_local_prefill": {"bytes": 2288012216, "source_digest": "855fe08802303e60"},
-    "chunk_prefill": {"bytes": 139947090, "source_digest": "855fe08802303e60"},
+    "mistral_prefill": {"bytes": 537737069, "source_digest": "285eee2a4d207be7"},
+    "sink_prefill": {"bytes": 1074167831, "source_digest": "285eee2a4d207be7"},
+    "gemma3_local_prefill": {"bytes": 2210386940, "source_digest": "285eee2a4d207be7"},
+    "chunk_prefill": {"bytes": 139827420, "source_digest": "285eee2a4d207be7"},
     "rolling_decode": {"bytes": 4300264727, "source_digest": "4243f18ace3b6e8a"},
     "gqa_decode": {"bytes": 1076055801, "source_digest": "4243f18ace3b6e8a"},
     "fp8_decode": {"bytes": 2151022590, "source_digest": "4243f18ace3b6e8a"},
