@@ -45,6 +45,11 @@ struct CacheF32 {
 struct CacheFp8 {  // OCP E4M3 bytes, 8 per lane: the same lane layout as bf16, twice the rows in flight
     static constexpr int kEPC = 8, kBytes = 8, kUnroll = 8;
 };
+struct CacheFp8W {  // OCP E4M3 bytes, 16 per lane (8 lanes per 128-byte row): one query head per workgroup
+    static constexpr int kEPC = 16, kBytes = 16, kUnroll = 4;
+};
+template <typename CK>
+constexpr bool is_fp8() { return std::is_same<CK, CacheFp8>::value || std::is_same<CK, CacheFp8W>::value; }
 
 template <typename CK, int D>
 struct DecodeCfg {
@@ -84,9 +89,10 @@ __device__ __forceinline__ void unpack(const typename DecodeCfg<CK, 64>::V &x, f
         f[3] = __uint_as_float(x.w);
     } else {
         typedef float f32x2 __attribute__((ext_vector_type(2)));
-        const uint32_t u[2] = {x.x, x.y};
+        constexpr int NW = sizeof(x) / 4;  // 32-bit words of 4 codes
+        const uint32_t *u = reinterpret_cast<const uint32_t *>(&x);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < NW; ++i) {
             const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)u[i], false);
             const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)u[i], true);
             f[4 * i + 0] = a.x;
@@ -136,7 +142,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     using CV = typename C::V;
     constexpr int EPC = C::kEPC, LPR = C::kLPR, RPI = C::kRPI, UN = C::kUnroll;
     constexpr bool kDot2 = std::is_same<QT, uint16_t>::value && std::is_same<CK, CacheBf16>::value;
-    constexpr bool kFp8 = std::is_same<CK, CacheFp8>::value;
+    constexpr bool kFp8 = is_fp8<CK>();
     __shared__ float sh_m[C::kGroups], sh_l[C::kGroups];
     __shared__ float sh_o[C::kGroups][D];
 
@@ -168,7 +174,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         const QT *q = reinterpret_cast<const QT *>(qp) + (size_t)(unit0 + j) * D + sub * EPC;
         if constexpr (std::is_same<QT, uint16_t>::value) {
             qx[j] = *reinterpret_cast<const uint4 *>(q);
-            if constexpr (!kDot2) unpack<CacheBf16>(qx[j], qf[j]);
+            if constexpr (!kDot2) {
+#pragma unroll
+                for (int e = 0; e < EPC; e += 8) unpack<CacheBf16>(*reinterpret_cast<const uint4 *>(q + e), &qf[j][e]);
+            }
         } else {
 #pragma unroll
             for (int e = 0; e < EPC; e += 4) {
@@ -723,7 +732,7 @@ static hipError_t launch_decode_t(const void *q, const void *kc, const void *vc,
                                   float sink_bias, void *ws, const float *ksc, const float *vsc,
                                   hipStream_t stream) {
     const int R = g + w;
-    const int kind = std::is_same<CK, CacheFp8>::value ? 1 : 0;
+    const int kind = is_fp8<CK>() ? 1 : 0;
     const int jobs = decode_jobs(batch, heads, kv_heads, kind);
     const int splits = decode_splits(jobs, R, kind);
     const int rps = (R + splits - 1) / splits;
@@ -753,7 +762,11 @@ static hipError_t launch_decode_d(const void *q, const void *kc, const void *vc,
             return hipErrorInvalidValue;
         case 4: return SWA_DEC(4);
         case 2: return SWA_DEC(2);
-        default: return SWA_DEC(1);
+        default:
+            if constexpr (std::is_same<CK, CacheFp8>::value && D == 128)
+                return launch_decode_t<QT, CacheFp8W, D, 1>(q, kc, vc, pos, o, lse, batch, heads, kv_heads, w, g,
+                                                            scale, sink_bias, ws, ksc, vsc, stream);
+            return SWA_DEC(1);
     }
 #undef SWA_DEC
 }
