@@ -76,9 +76,9 @@ MEASURED_TRAFFIC = {
     "sink_prefill": {"bytes": 1074167831, "source_digest": "285eee2a4d207be7"},
     "gemma3_local_prefill": {"bytes": 2210386940, "source_digest": "285eee2a4d207be7"},
     "chunk_prefill": {"bytes": 139827420, "source_digest": "285eee2a4d207be7"},
-    "rolling_decode": {"bytes": 4300264727, "source_digest": "4243f18ace3b6e8a"},
-    "gqa_decode": {"bytes": 1076055801, "source_digest": "4243f18ace3b6e8a"},
-    "fp8_decode": {"bytes": 2151022590, "source_digest": "4243f18ace3b6e8a"},
+    "rolling_decode": {"bytes": 4300265431, "source_digest": "1197048432c9c06b"},
+    "gqa_decode": {"bytes": 1076057369, "source_digest": "1197048432c9c06b"},
+    "fp8_decode": {"bytes": 2151013950, "source_digest": "1197048432c9c06b"},
 }
 CSRC = os.path.join(ROOT, "block_sparse_causal_band_amd", "csrc")
 
