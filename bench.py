@@ -377,7 +377,7 @@ def bench_decode(name, steps, warmup):
                    "positions": [lo, hi], "kv_bytes_per_step": nbytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel": ("decode_kernel<bf16,fp8,128>" if fp8 else
+                     "kernel": ("decode_kernel<bf16,fp8x16,128>" if fp8 else
                                 "decode_mfma_kernel<128>" if Hkv < H else "decode_kernel<bf16,bf16,128>"),
                      "avg_launch_ms": ms_launch, "min_launch_ms": min(per)},
     }
