@@ -29,7 +29,8 @@ hipError_t launch_dilated_prefill(const void *q, const void *k, const void *v, v
                                   hipStream_t stream);
 hipError_t launch_landmark_part(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
                                 int heads, int kv_heads, int n, int d, int w, int g, int r, float scale, bool bf16,
-                                hipStream_t stream);
+                                hipStream_t stream, void *merge_o = nullptr, const float *merge_lse = nullptr,
+                                float *merged_lse = nullptr);
 hipError_t launch_kv_append_fp8(void *kc, void *vc, const void *kn, const void *vn, const int64_t *pos,
                                 const float *ksc, const float *vsc, int batch, int heads, int tn, int d, int w,
                                 int g, bool bf16, hipStream_t stream);
@@ -153,9 +154,10 @@ size_t swa_landmark_workspace_bytes(int batch, int heads, int n, int d, swa_dtyp
     if (batch < 1 || heads < 1 || n < 1 || (d != 64 && d != 128) || (dtype != SWA_F32 && dtype != SWA_BF16))
         return 0;
     const size_t rows = (size_t)batch * heads * n;
-    const size_t ob = (rows * d * (dtype == SWA_BF16 ? 2 : 4) + 255) / 256 * 256;
     const size_t lb = (rows * 4 + 255) / 256 * 256;
-    return ob + 2 * lb;
+    if (dtype == SWA_BF16) return lb;  // the window part's LSE (the landmark part merges in its epilogue)
+    const size_t ob = (rows * d * 4 + 255) / 256 * 256;
+    return ob + 2 * lb;  // fp32: the landmark part's o and both LSEs, merged by a third launch
 }
 
 int swa_landmark_prefill_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int batch, int heads,
@@ -170,6 +172,17 @@ int swa_landmark_prefill_fwd(const void *q, const void *k, const void *v, void *
     const bool bf16 = dtype == SWA_BF16;
     const size_t rows = (size_t)batch * heads * n;
     uint8_t *ws = static_cast<uint8_t *>(workspace);
+    if (bf16) {
+        // window and sinks into o (its LSE into the workspace), then the
+        // landmark part, merged into o by LSE in its own epilogue
+        float *lse_a = reinterpret_cast<float *>(ws);
+        hipError_t e = swa::launch_prefill(q, k, v, o, lse_a, batch, heads, kv_heads, n, d, w, g, scale, sink_bias,
+                                           true, stream);
+        if (e == hipSuccess)
+            e = swa::launch_landmark_part(q, k, v, o, nullptr, batch, heads, kv_heads, n, d, w, g, r, scale, true,
+                                          stream, o, lse_a, lse);
+        return status_of(e);
+    }
     void *o_b = ws;
     float *lse_a = reinterpret_cast<float *>(ws + (rows * d * (bf16 ? 2 : 4) + 255) / 256 * 256);
     float *lse_b = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(lse_a) + (rows * 4 + 255) / 256 * 256);

@@ -111,6 +111,11 @@ struct PathArgs {
     int part;              // chunk: which keys
     int r;                 // strided: the stride
     int mode;              // strided: 1 dilated, 2 landmark part
+    // landmark part (bf16) merged into the window part's result: o of the
+    // window part, merged in place; its LSE; where the merged LSE goes (or null)
+    uint16_t *mo;
+    const float *mla;
+    float *mlo;
 };
 constexpr int kNoWindow = 1 << 30;  // a window wider than any sequence
 
@@ -236,6 +241,64 @@ __device__ __forceinline__ void store_rows_lds(const f32x16 (&oacc)[D / 32], flo
     }
     const int qi = qw0 + lr;
     if (lse != nullptr && lh == 0 && qi < nq) lse[(size_t)qi * rs] = m_run * scale + logf(l_tot);
+}
+
+// The landmark part of a landmark launch, merged in its epilogue into the
+// window part's result by LSE, with the arithmetic of lse_merge_kernel: the
+// rows of this part are staged in LDS as bf16 exactly as store_rows_lds
+// writes them, with their LSE m * scale + ln l (-inf where the row has no
+// landmark); each lane then merges 8 values of a row with the window part's
+// o and LSE and writes o (in place) and the merged LSE.
+template <int D>
+__device__ __forceinline__ void merge_rows_lds(const f32x16 (&oacc)[D / 32], float m_run, float l_run, int qw0,
+                                               int nq, int lr, int lh, int lane, uint16_t *O, const float *la,
+                                               float *lo, float scale, uint8_t *region, float *lreg) {
+    constexpr int RB = 2 * D;
+    constexpr int CPR = RB / 16;
+    const float l_tot = half_swap_sum(l_run);
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            const int ch = 4 * cb + gq;
+            const float x0 = oacc[cb][4 * gq + 0] * inv, x1 = oacc[cb][4 * gq + 1] * inv;
+            const float x2 = oacc[cb][4 * gq + 2] * inv, x3 = oacc[cb][4 * gq + 3] * inv;
+            *reinterpret_cast<uint2 *>(region + lr * RB + ((ch ^ (lr % CPR)) * 16) + 8 * lh) =
+                make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
+        }
+    if (lh == 0) lreg[lr] = m_run * scale + logf(l_tot);
+#pragma unroll
+    for (int j = 0; j < 32 * CPR / 64; ++j) {
+        const int idx = 64 * j + lane;
+        const int r = idx / CPR, ch = idx % CPR;
+        const int row = qw0 + r;
+        if (row >= nq) continue;
+        const uint4 vb = *reinterpret_cast<const uint4 *>(region + r * RB + ((ch ^ (r % CPR)) * 16));
+        const float a = la[row], b = lreg[r];
+        const float M = fmaxf(a, b);
+        float wa = 0.f, wb = 0.f;
+        if (M != kNegInf) {
+            wa = fast_exp2((a - M) * (float)kLog2e);
+            wb = fast_exp2((b - M) * (float)kLog2e);
+        }
+        const float sum = wa + wb;
+        const float sinv = (sum > 0.f) ? 1.f / sum : 0.f;
+        wa *= sinv;
+        wb *= sinv;
+        uint16_t *orow = O + (size_t)row * D + 8 * ch;
+        const uint4 va = *reinterpret_cast<const uint4 *>(orow);
+        const uint32_t ua[4] = {va.x, va.y, va.z, va.w}, ub[4] = {vb.x, vb.y, vb.z, vb.w};
+        uint32_t res[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float r0 = (wa > 0.f ? wa * bf16lo(ua[e]) : 0.f) + (wb > 0.f ? wb * bf16lo(ub[e]) : 0.f);
+            const float r1 = (wa > 0.f ? wa * bf16hi(ua[e]) : 0.f) + (wb > 0.f ? wb * bf16hi(ub[e]) : 0.f);
+            res[e] = pack_bf16x2(r0, r1);
+        }
+        *reinterpret_cast<uint4 *>(orow) = make_uint4(res[0], res[1], res[2], res[3]);
+        if (lo != nullptr && ch == 0) lo[row] = (sum > 0.f) ? M + logf(sum) : kNegInf;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -619,6 +682,14 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     // stages its rows in its own 32 * 2D bytes of the K buffers
     static_assert(2 * 32 * 2 * D <= L::kTileBytes, "two waves' rows per K buffer");
     uint8_t *const region = ((wave < 2) ? kbuf0 : kbuf1) + (wave & 1) * (32 * 2 * D);
+    if constexpr (STRIDED) {
+        if (ca.mode == 2 && ca.mo != nullptr) {
+            merge_rows_lds<D>(oacc, m_run, l_run, q0 + wave * 32, nq, lr, lh, lane, ca.mo + base,
+                              ca.mla + (size_t)unit * n, ca.mlo ? ca.mlo + (size_t)unit * n : nullptr, scale, region,
+                              reinterpret_cast<float *>(vbuf0) + 32 * wave);
+            return;
+        }
+    }
     store_rows_lds<D>(oacc, m_run, l_run, q0 + wave * 32, nq, lr, lh, lane, op + base + (size_t)oq * D,
                       lsep ? lsep + (size_t)unit * n + oq : nullptr, scale, sq, region);
 }
@@ -937,12 +1008,17 @@ hipError_t launch_dilated_prefill(const void *q, const void *k, const void *v, v
 }
 
 // Landmark part of window + sinks + landmarks every r: the landmarks below
-// the window and not below g (lse of rows without one: -inf, o = 0).
+// the window and not below g (lse of rows without one: -inf, o = 0).  With
+// merge_o set (bf16 only) the part is not stored but merged by LSE into the
+// window part's result: merge_o (o, in place) and merge_lse, the merged LSE
+// going to merged_lse when that is not null (o and lse are then unused).
 hipError_t launch_landmark_part(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
                                 int heads, int kv_heads, int n, int d, int w, int g, int r, float scale, bool bf16,
-                                hipStream_t stream) {
-    return launch_prefill_t<kStrided>(q, k, v, o, lse, batch, heads, kv_heads, n, d, w, g, scale, 0.f, bf16,
-                                      PathArgs{nullptr, nullptr, nullptr, 0, r, 2}, 1, n, stream);
+                                hipStream_t stream, void *merge_o, const float *merge_lse, float *merged_lse) {
+    return launch_prefill_t<kStrided>(
+        q, k, v, o, lse, batch, heads, kv_heads, n, d, w, g, scale, 0.f, bf16,
+        PathArgs{nullptr, nullptr, nullptr, 0, r, 2, static_cast<uint16_t *>(merge_o), merge_lse, merged_lse}, 1, n,
+        stream);
 }
 
 // ---------------------------------------------------------------------------

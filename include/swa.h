@@ -241,8 +241,10 @@ int swa_decode_fwd_fp8(const void *q, const void *k_cache, const void *v_cache,
  * swa_landmark_prefill_fwd: query i reads its window i-w+1 .. i, the sinks
  * 0 .. g-1 and the landmarks, every position j <= i with j mod r == 0, each
  * position once; sink_bias on positions < g.  Computed as the window-and-
- * sinks part into o, the part over the landmarks below the window and not
- * below g into the workspace, and an LSE merge (swa_lse_merge) into o.
+ * sinks part into o, then the part over the landmarks below the window and
+ * not below g, merged by LSE (the arithmetic of swa_lse_merge) into o: for
+ * bf16 in the landmark launch's own epilogue (the workspace holds the first
+ * part's LSE), for fp32 through the workspace and a merge launch.
  * workspace: at least swa_landmark_workspace_bytes(...) bytes, 16-byte
  * aligned (SWA_EWORKSPACE otherwise).
  */

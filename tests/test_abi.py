@@ -258,8 +258,10 @@ def test_landmark_rejects(kw, want):
 
 
 def test_landmark_workspace_size():
-    # o of the landmark part (bf16) plus two fp32 lse rows, each rounded up to 256 bytes
-    assert swa.landmark_workspace_bytes(1, 2, 64, 128, 1) == 1 * 2 * 64 * 128 * 2 + 2 * 512
+    # bf16: the window part's fp32 lse rows, rounded up to 256 bytes (the landmark
+    # part merges in its epilogue); fp32: the landmark part's o plus two lse rows
+    assert swa.landmark_workspace_bytes(1, 2, 64, 128, 1) == 512
+    assert swa.landmark_workspace_bytes(1, 2, 64, 128, 0) == 1 * 2 * 64 * 128 * 4 + 2 * 512
     assert swa.landmark_workspace_bytes(1, 2, 64, 96, 1) == 0
 
 

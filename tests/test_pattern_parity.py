@@ -75,6 +75,18 @@ def test_landmark_vs_oracle(dtype, d, n, w, g, r, beta):
     _check(q, k, v, o, lse, "landmark", w, g, r, beta)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_landmark_without_lse_output(d):
+    """Without an LSE output the window part's LSE goes to the workspace; o is
+    the same bit for bit."""
+    dev = _dev()
+    q, k, v = synth.qkv(2, 2, 517, d, torch.bfloat16, seed=95, device=dev)
+    a, _ = swa.landmark_prefill(q, k, v, w=64, g=4, r=32, sink_bias=2.0, return_lse=True)
+    b = swa.landmark_prefill(q, k, v, w=64, g=4, r=32, sink_bias=2.0)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("kind", ["dilated", "landmark"])
 def test_patterns_gqa(kind):
     dev = _dev()
