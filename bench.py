@@ -72,10 +72,10 @@ PATTERN = {
 # the source has changed since, the figure no longer describes the kernel and
 # `traffic` is reported as null.
 MEASURED_TRAFFIC = {
-    "mistral_prefill": {"bytes": 537737069, "source_digest": "285eee2a4d207be7"},
-    "sink_prefill": {"bytes": 1074167831, "source_digest": "285eee2a4d207be7"},
-    "gemma3_local_prefill": {"bytes": 2210386940, "source_digest": "285eee2a4d207be7"},
-    "chunk_prefill": {"bytes": 139827420, "source_digest": "285eee2a4d207be7"},
+    "mistral_prefill": {"bytes": 537654927, "source_digest": "f4050d4cfde5a500"},
+    "sink_prefill": {"bytes": 1074220565, "source_digest": "f4050d4cfde5a500"},
+    "gemma3_local_prefill": {"bytes": 2226296863, "source_digest": "f4050d4cfde5a500"},
+    "chunk_prefill": {"bytes": 140024216, "source_digest": "f4050d4cfde5a500"},
     "rolling_decode": {"bytes": 4300265431, "source_digest": "1197048432c9c06b"},
     "gqa_decode": {"bytes": 1076057369, "source_digest": "1197048432c9c06b"},
     "fp8_decode": {"bytes": 2151013950, "source_digest": "1197048432c9c06b"},
@@ -301,7 +301,7 @@ def bench_pattern(name, steps, warmup):
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
                      "kernel": ("prefill_bf16_kernel<128,4,strided> (dilated classes)" if kind == "dilated" else
-                                "window prefill + landmark part + lse_merge (one call)"),
+                                "window prefill + landmark part merged in its epilogue (one call)"),
                      "avg_launch_ms": ms_launch, "min_launch_ms": min(per)},
     }
 
