@@ -492,8 +492,8 @@ def main():
                     help="run only a 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(heads and batch shard with no exchange; see the design notes). Use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(heads and batch would shard with no exchange between GPUs). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
