@@ -101,3 +101,16 @@ def test_workgroup_order_runs_blocks_first_to_last():
         for u in np.unique(run[:, 0]):
             qbs = run[run[:, 0] == u, 1]
             assert np.all(np.diff(qbs) == 1) and qbs[0] == 0
+
+
+def test_schedule_random_shapes(orc):
+    """The same checks over random shapes (seeded): ragged n, windows narrower
+    and wider than a tile or the sequence, sinks below, inside and beyond the
+    first tile."""
+    rng = np.random.default_rng(2024)
+    for _ in range(60):
+        n = int(rng.integers(1, 400))
+        w = int(rng.integers(1, 450))
+        g = int(rng.integers(0, 80))
+        bq, bk = TILES[int(rng.integers(0, len(TILES)))]
+        _check(orc, n, w, g, bq, bk)
