@@ -124,6 +124,25 @@ def test_decode_gqa_split_and_unsplit(orc, B, H, Hkv):
     _decode_gqa_vs_oracle(orc, q, kc, vc, pos, w, g, 0.0, units=units)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_decode_random_shapes(orc, dtype):
+    """Seeded random decode problems: ring sizes, sink counts, head groupings
+    (one to eight query heads per key/value head), head sizes and positions
+    before, at and far past the ring's wrap."""
+    dev = _dev()
+    rng = np.random.default_rng(78)
+    for case in range(8):
+        w = int(rng.integers(1, 300))
+        g = int(rng.integers(0, 20))
+        d = int(rng.choice([64, 128]))
+        H, Hkv = [(1, 1), (4, 4), (8, 2), (8, 1), (6, 3), (16, 2), (2, 1), (5, 5)][case]
+        B = int(rng.integers(1, 5))
+        q, kc, vc, _ = synth.decode_problem(B, H, d, g + w, 0, 0, dtype, seed=200 + case, device=dev, kv_heads=Hkv)
+        positions = [int(x) for x in rng.integers(0, 4 * w + g + 2, B)]
+        pos = torch.tensor(positions, dtype=torch.int64, device=dev)
+        _decode_gqa_vs_oracle(orc, q, kc, vc, pos, w, g, float(rng.uniform(-1.0, 3.0)))
+
+
 def test_decode_gqa_through_appended_cache(orc):
     """kv_append writes Hkv heads; decode of H query heads reads them."""
     dev = _dev()
