@@ -144,6 +144,7 @@ int swa_dilated_prefill_fwd(const void *q, const void *k, const void *v, void *o
                             int kv_heads, int n, int d, int w, int r, float scale, swa_dtype_t dtype,
                             hipStream_t stream) {
     if (r < 1) return SWA_EINVAL;
+    if (n >= 1 && r > n) r = n;  // every stride >= n reads the same keys (each query only itself)
     int st = check_prefill(q, k, v, o, lse, batch, heads, kv_heads, n, d, w, 0, scale, 0.f, dtype, r);
     if (st != SWA_OK) return st;
     return status_of(swa::launch_dilated_prefill(q, k, v, o, lse, batch, heads, kv_heads, n, d, w, r, scale,
@@ -164,6 +165,7 @@ int swa_landmark_prefill_fwd(const void *q, const void *k, const void *v, void *
                              int kv_heads, int n, int d, int w, int g, int r, float scale, float sink_bias,
                              swa_dtype_t dtype, void *workspace, size_t workspace_bytes, hipStream_t stream) {
     if (r < 1) return SWA_EINVAL;
+    if (n >= 1 && r > n) r = n;  // every stride >= n has the one landmark 0
     int st = check_prefill(q, k, v, o, lse, batch, heads, kv_heads, n, d, w, g, scale, sink_bias, dtype, 1);
     if (st != SWA_OK) return st;
     const size_t need = swa_landmark_workspace_bytes(batch, heads, n, d, dtype);

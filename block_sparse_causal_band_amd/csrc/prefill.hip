@@ -119,6 +119,15 @@ struct PathArgs {
 };
 constexpr int kNoWindow = 1 << 30;  // a window wider than any sequence
 
+// Byte offset of row `row` of a buffer of n rows, the row index formed in 64
+// bits and clamped to n: a row at or past n reads as zero through the buffer
+// range check, and no stride product can wrap round 2^32 back into range
+// (n rows plus any 16-byte chunk of a row fit in 32 bits, n * row_bytes being
+// below 2^32).
+__device__ __forceinline__ uint32_t row_off(uint64_t row, int n, uint32_t row_bytes) {
+    return (uint32_t)(row < (uint64_t)n ? row : (uint64_t)n) * row_bytes;
+}
+
 // Cache row of key position s < p0 (s >= 0).
 __device__ __forceinline__ int cache_row(int s, int p0, int w, int g) {
     return (s >= p0 - w) ? g + s % w : s;
@@ -421,7 +430,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     {
         const int qr0 = oq + q0 * sq;  // first row of this block in q
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + (size_t)qr0 * D, (uint32_t)(n - qr0) * L::kRowBytes);
-        const uint32_t rowoff = (uint32_t)((wave * 32 + lr) * sq) * L::kRowBytes;
+        const uint32_t rowoff = row_off((uint64_t)(wave * 32 + lr) * sq, n, L::kRowBytes);
 #pragma unroll
         for (int c = 0; c < D / 16; ++c)
             qf[c] = __builtin_bit_cast(bf16x8, buffer_load16(rq, rowoff + (16 * c + 8 * lh) * 2));
@@ -441,8 +450,12 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
         const int pos = lane & 3;
         const int ck = (m >> 2) * 4 + (pos ^ ((key >> 2) & 3));
         const int cv = (m >> 2) * 4 + pos;
-        dma_k[i] = key * skv * L::kRowBytes + 16 * ck;
-        dma_v[i] = key * skv * L::kRowBytes + 16 * cv;
+        // strided rows: the 64-bit, clamped offset (a stride can be as large
+        // as n); otherwise key * row bytes, from which the chunk gather below
+        // recovers the key
+        const uint32_t rb = STRIDED ? row_off((uint64_t)key * skv, n, L::kRowBytes) : key * L::kRowBytes;
+        dma_k[i] = rb + 16 * ck;
+        dma_v[i] = rb + 16 * cv;
     }
     auto dma_rows = [&](const uint16_t *src, const uint32_t *offs, int r0, int nrows, uint8_t *dst) {
         // rows r0 .. of src, rows >= nrows read as zero
@@ -720,7 +733,7 @@ struct F32KeyRows {
     __device__ __forceinline__ uint4 load(bool is_k, int s, int col_byte, int d) const {
         if (!chunk || s >= p0) {
             const __amdgpu_buffer_rsrc_t r = make_rsrc(is_k ? k : v, (uint32_t)n * d * 4);
-            return buffer_load16(r, (uint32_t)(okv + (s - p0) * skv) * d * 4 + col_byte);
+            return buffer_load16(r, row_off((uint64_t)okv + (uint64_t)(s - p0) * skv, n, d * 4) + col_byte);
         }
         const __amdgpu_buffer_rsrc_t r = make_rsrc(is_k ? kc : vc, (uint32_t)(g + w) * d * 4);
         return buffer_load16(r, (uint32_t)cache_row(s, p0, w, g) * d * 4 + col_byte);
@@ -857,7 +870,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
     {
         const int qr0 = oq + q0 * sq;
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + (size_t)qr0 * D, (uint32_t)(n - qr0) * D * 4);
-        const uint32_t rowoff = (uint32_t)((wave * 32 + lr) * sq) * D * 4;
+        const uint32_t rowoff = row_off((uint64_t)(wave * 32 + lr) * sq, n, D * 4);
 #pragma unroll
         for (int c4 = 0; c4 < D / 8; ++c4) {
             const uint4 a = buffer_load16(rq, rowoff + (8 * c4) * 4);

@@ -77,6 +77,11 @@ enum {
  * Only the key tiles that hold attended pairs are visited (the diagonal band
  * plus the sink tiles below it); nothing n x n is ever formed.  K and V rows
  * at positions >= n are never read.
+ * Inputs must be finite at every position < n.  A key that one query of a
+ * visited tile attends and another does not still enters the second query's
+ * value product, with a probability of exactly 0; an Inf or NaN in that key's
+ * V row would turn 0 into NaN there (0 * Inf), so non-finite K or V rows can
+ * reach output rows that do not attend them.
  */
 int swa_prefill_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                     int batch, int heads, int n, int d, int w, int g,

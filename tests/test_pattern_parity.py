@@ -10,6 +10,7 @@ import block_sparse_causal_band_amd as swa
 import oracle
 from block_sparse_causal_band_amd import synth
 from oracle import patterns
+from tests.parity import gate
 
 pytestmark = pytest.mark.gpu
 
@@ -36,10 +37,8 @@ def _check(q, k, v, o, lse, kind, w, g, r, beta, rows=None):
             gl = lse[b, h].cpu().numpy()
             if rows is not None:
                 go, gl = go[rows], gl[rows]
-            assert np.all(np.isfinite(go))
-            err = float(np.max(np.abs(go - ro)))
-            assert err <= tol, f"{kind} b{b} h{h}: max-abs {err:.3g}"
-            assert float(np.max(np.abs(gl - rl))) <= tol
+            gate(go, ro, q.dtype, f"{kind} b{b} h{h}", tol=tol)
+            gate(gl, rl, q.dtype, f"{kind} lse", tol=tol)
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -117,3 +116,26 @@ def test_patterns_full_size_sampled(kind):
     torch.cuda.synchronize()
     rows = sorted(set(np.random.default_rng(95).integers(0, n, 64).tolist()) | {0, n - 1})
     _check(q[:, :4], k[:, :4], v[:, :4], o[:, :4], lse[:, :4], kind, w, g, r, beta, rows=rows)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("kind", ["dilated", "landmark"])
+def test_huge_stride_equals_stride_n(dtype, kind):
+    """Any stride r >= n reads the same keys as r = n (dilated: each query only
+    itself; landmarks: position 0 only), so a stride far past n -- whose row
+    offsets would overflow 32 bits -- gives the r = n result bit for bit, and
+    the oracle's."""
+    dev = _dev()
+    n, w, g = 300, 16, 2
+    q, k, v = synth.qkv(1, 2, n, 128, dtype, seed=96, device=dev)
+    outs = []
+    for r in (n, 2 ** 20, 2 ** 30):
+        if kind == "dilated":
+            outs.append(swa.dilated_prefill(q, k, v, w=w, r=r, return_lse=True))
+        else:
+            outs.append(swa.landmark_prefill(q, k, v, w=w, g=g, r=r, sink_bias=1.0, return_lse=True))
+    torch.cuda.synchronize()
+    for o, lse in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
+    gg, beta = (0, 0.0) if kind == "dilated" else (g, 1.0)
+    _check(q, k, v, outs[-1][0], outs[-1][1], kind, w, gg, 2 ** 30, beta)
