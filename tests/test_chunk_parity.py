@@ -19,6 +19,7 @@ import block_sparse_causal_band_amd as swa
 import oracle
 from block_sparse_causal_band_amd import synth
 from oracle import cache_model
+from tests.parity import gate
 
 pytestmark = pytest.mark.gpu
 
@@ -93,10 +94,8 @@ def test_chunk_vs_oracle(orc, dtype, d, w, g, beta, T, p0s):
     torch.cuda.synchronize()
     ro, rl = _oracle_rows(orc, q, kseq, vseq, p0s, T, w, g, beta)
     go = o.float().cpu().numpy()
-    assert np.all(np.isfinite(go)), "non-finite output: an unwritten cache row was read"
-    err = float(np.max(np.abs(go - ro)))
-    assert err <= _tol(dtype), f"max-abs {err:.3g}"
-    assert float(np.max(np.abs(lse.cpu().numpy() - rl))) <= _tol(dtype)
+    gate(go, ro, dtype, f"chunk w={w} g={g} T={T} d={d}")
+    gate(lse.cpu().numpy(), rl, dtype, "chunk lse")
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -107,7 +106,7 @@ def test_chunk_gqa_vs_oracle(orc, dtype):
     o = swa.chunk_prefill(q.to(dev), kn.to(dev), vn.to(dev), kc, vc, pos, w=w, g=g, sink_bias=1.0)
     torch.cuda.synchronize()
     ro, _ = _oracle_rows(orc, q, kseq, vseq, p0s, T, w, g, 1.0)
-    assert float(np.max(np.abs(o.float().cpu().numpy() - ro))) <= _tol(dtype)
+    gate(o.float().cpu().numpy(), ro, dtype, "chunk gqa")
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -124,8 +123,8 @@ def test_partials_merge_to_full(orc, dtype):
     om, lm = swa.lse_merge(oc, lc, on, ln)
     torch.cuda.synchronize()
     ro, rl = _oracle_rows(orc, q, kseq, vseq, p0s, T, w, g, beta)
-    assert float(np.max(np.abs(om.float().cpu().numpy() - ro))) <= _tol(dtype)
-    assert float(np.max(np.abs(lm.cpu().numpy() - rl))) <= _tol(dtype)
+    gate(om.float().cpu().numpy(), ro, dtype, "chunk partials merged")
+    gate(lm.cpu().numpy(), rl, dtype, "chunk partials merged lse")
     # rows whose window lies inside the chunk and whose sinks are too (or g = 0 reached): no cache key
     lc_h, oc_h = lc.cpu().numpy(), oc.float().cpu().numpy()
     for b, p0 in enumerate(p0s):
@@ -236,5 +235,5 @@ def test_chunk_full_size_sampled(orc):
     ro, rl = orc.decode(torch.stack(qs), ps, np.stack(kps), torch.stack(ks), torch.stack(vs), w=w, g=g)
     go = torch.stack([o[0, h, i] for h, i in samples]).float().cpu().numpy()
     gl = torch.stack([lse[0, h, i] for h, i in samples]).cpu().numpy()
-    assert float(np.max(np.abs(go - ro))) <= BF16_TOL
-    assert float(np.max(np.abs(gl - rl))) <= BF16_TOL
+    gate(go, ro, torch.bfloat16, f"chunk full size, {len(samples)} sampled rows")
+    gate(gl, rl, torch.bfloat16, "chunk full size lse")

@@ -15,6 +15,7 @@ import block_sparse_causal_band_amd as swa
 import oracle
 from block_sparse_causal_band_amd import synth
 from oracle import cache_model, fp8
+from tests.parity import gate
 
 pytestmark = pytest.mark.gpu
 
@@ -99,10 +100,8 @@ def _decode_fp8_vs_oracle(orc, q, kc, vc, ks, vs, pos, w, g, beta, units=None):
     ro, rl = orc.decode(np.stack(qs), ps, np.stack(kps), np.stack(kk_l), np.stack(vv_l), w=w, g=g, beta=beta)
     go = torch.stack([o[b, h] for b, h in units]).float().cpu().numpy()
     gl = torch.stack([lse[b, h] for b, h in units]).cpu().numpy()
-    assert np.all(np.isfinite(go))
-    err = float(np.max(np.abs(go - ro)))
-    assert err <= _tol(q.dtype), f"decode_fp8 max-abs {err:.3g}"
-    assert float(np.max(np.abs(gl - rl))) <= _tol(q.dtype)
+    err, _ = gate(go, ro, q.dtype, f"fp8 decode H={H} Hkv={Hkv} w={w} g={g}")
+    gate(gl, rl, q.dtype, "fp8 decode lse")
     return err
 
 

@@ -16,6 +16,7 @@ import block_sparse_causal_band_amd as swa
 import oracle
 from block_sparse_causal_band_amd import synth
 from oracle import cache_model
+from tests.parity import gate
 
 pytestmark = pytest.mark.gpu
 
@@ -45,10 +46,8 @@ def test_prefill_gqa_vs_oracle(orc, dtype, d, H, Hkv):
     for b in range(B):
         ro, rl = orc.prefill(q[b], k[b], v[b], w=w, g=g, beta=beta)
         go = o[b].float().cpu().numpy()
-        assert np.all(np.isfinite(go))
-        err = float(np.max(np.abs(go - ro)))
-        assert err <= _tol(dtype), f"max-abs {err:.3g} (H={H}, Hkv={Hkv}, {dtype}, d={d})"
-        assert float(np.max(np.abs(lse[b].cpu().numpy() - rl))) <= _tol(dtype)
+        gate(go, ro, dtype, f"gqa prefill b={b} H={H} Hkv={Hkv} d={d}")
+        gate(lse[b].cpu().numpy(), rl, dtype, "gqa prefill lse")
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -90,10 +89,8 @@ def _decode_gqa_vs_oracle(orc, q, kc, vc, pos, w, g, beta, units=None):
     ro, rl = orc.decode(torch.stack(qs), ps, np.stack(kps), torch.stack(ks), torch.stack(vs), w=w, g=g, beta=beta)
     go = torch.stack([o[b, h] for b, h in units]).float().cpu().numpy()
     gl = torch.stack([lse[b, h] for b, h in units]).cpu().numpy()
-    assert np.all(np.isfinite(go))
-    err = float(np.max(np.abs(go - ro)))
-    assert err <= _tol(q.dtype), f"decode max-abs {err:.3g} (H={H}, Hkv={Hkv})"
-    assert float(np.max(np.abs(gl - rl))) <= _tol(q.dtype)
+    err, _ = gate(go, ro, q.dtype, f"gqa decode H={H} Hkv={Hkv} w={w} g={g}")
+    gate(gl, rl, q.dtype, "gqa decode lse")
     return err
 
 
