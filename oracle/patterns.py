@@ -36,13 +36,6 @@ def read_set(i: int, kind: str, w: int, g: int = 0, r: int = 1) -> set[int]:
     return s
 
 
-def mask(n: int, kind: str, w: int, g: int = 0, r: int = 1) -> np.ndarray:
-    m = np.zeros((n, n), dtype=bool)
-    for i in range(n):
-        m[i, sorted(read_set(i, kind, w, g, r))] = True
-    return m
-
-
 def prefill(q, k, v, kind: str, w: int, g: int = 0, r: int = 1, scale: float | None = None, beta: float = 0.0,
             rows=None):
     """q, k, v: [n, d] (one head; K/V already matched to the query head).

@@ -9,8 +9,8 @@
  *
  *  [P3] "Sliding Window and Sparse Attention, from Longformer to CSA2"
  *       section 1 (attention = softmax(Q K^T / sqrt(d)) V, causal j <= i),
- *       section 2 (window of the most recent w keys, positions i-w+1 .. i;
- *       attention sinks: the first g tokens stay readable),
+ *       section 2 (the window: key positions i-w+1 .. i, w of them counting
+ *       i itself; sinks: positions 0 .. g-1 are kept readable for good),
  *       section 10 glossary "LSE" (the softmax normaliser).
  *  [P4] "Local and Sparse Attention: Reading Fewer Token Positions"
  *       Figure 1 (window of 3 = current position plus the two before it),
