@@ -6,6 +6,7 @@ behind the C ABI of include/swa.h); this package is its thin Python binding.
     from block_sparse_causal_band_amd import prefill, kv_append, decode
     from block_sparse_causal_band_amd import chunk_prefill, lse_merge
     from block_sparse_causal_band_amd import kv_append_fp8, decode_fp8
+    from block_sparse_causal_band_amd import decode_noalloc
     from block_sparse_causal_band_amd import dilated_prefill, landmark_prefill
 
 Importing the package does not load the library; the first call does, and
@@ -19,6 +20,8 @@ from .binding import (  # noqa: F401
     chunk_prefill,
     decode,
     decode_fp8,
+    decode_noalloc,
+    decode_scratch_bytes,
     decode_workspace_bytes,
     dilated_prefill,
     kv_append,

@@ -62,6 +62,11 @@ def lib() -> ctypes.CDLL:
         L.swa_decode_fwd_gqa.restype = _int
         L.swa_decode_workspace_bytes_gqa.argtypes = [_int] * 6
         L.swa_decode_workspace_bytes_gqa.restype = ctypes.c_size_t
+        L.swa_decode_fwd_gqa_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int,
+                                                 _int, _flt, _flt, _int, _vp]
+        L.swa_decode_fwd_gqa_noalloc.restype = _int
+        L.swa_decode_scratch_bytes.argtypes = []
+        L.swa_decode_scratch_bytes.restype = ctypes.c_size_t
         L.swa_chunk_prefill_fwd.argtypes = [_vp] * 8 + [_int] * 7 + [ctypes.c_float] * 2 + [_int, _int, _vp]
         L.swa_chunk_prefill_fwd.restype = _int
         L.swa_kv_append_fp8.argtypes = [_vp] * 7 + [_int] * 6 + [_int, _vp]
@@ -278,6 +283,40 @@ def decode(q, k_cache, v_cache, pos, w: int, g: int = 0, scale: float | None = N
     if rc != 0:
         raise SwaError(rc, "swa_decode_fwd_gqa")
     return (o, lse) if return_lse else o
+
+
+def decode_noalloc(q, k_cache, v_cache, pos, w: int, g: int = 0, scale: float | None = None,
+                   sink_bias: float = 0.0, lse=None, out=None):
+    """decode() through the entry point that allocates nothing: `out` (and
+    `lse`, fp32 [batch, heads], if given) must be passed in, and a split
+    launch keeps its partial results in the library's fixed device scratch
+    (calls that overlap in time on one device race on it)."""
+    import torch
+
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("pos", pos), ("out", out)):
+        _dev_tensor(t, name)
+    B, H, d = q.shape
+    _need(k_cache.dim() == 4, "caches must be [batch, kv_heads, g + w, d]")
+    Hkv = k_cache.shape[1]
+    _need(k_cache.shape == v_cache.shape == (B, Hkv, g + w, d), "caches must be [batch, kv_heads, g + w, d]")
+    _need(q.dtype == k_cache.dtype == v_cache.dtype, "one dtype for q and the caches")
+    _need(pos.dtype == torch.int64 and pos.shape == (B,), "pos must be int64 [batch]")
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    if lse is not None:
+        _dev_tensor(lse, "lse")
+        _need(lse.shape == (B, H) and lse.dtype == torch.float32, "lse must be fp32 [batch, heads]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    rc = lib().swa_decode_fwd_gqa_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), pos.data_ptr(),
+                                          out.data_ptr(), lse.data_ptr() if lse is not None else None, B, H, Hkv, d,
+                                          int(w), int(g), float(scale), float(sink_bias), _dtype_code(q), _stream(q))
+    if rc != 0:
+        raise SwaError(rc, "swa_decode_fwd_gqa_noalloc")
+    return out
+
+
+def decode_scratch_bytes() -> int:
+    return int(lib().swa_decode_scratch_bytes())
 
 
 def _prefill_shapes(q, k, v):

@@ -40,6 +40,10 @@ hipError_t launch_decode_fp8(const void *q, const void *kc, const void *vc, cons
 hipError_t launch_lse_merge(const void *oa, const float *la, const void *ob, const float *lb, void *o, float *lse,
                             long rows, int d, bool bf16, hipStream_t stream);
 int prefill_rows_per_workgroup(bool bf16);
+hipError_t launch_decode_noalloc(const void *q, const void *kc, const void *vc, const int64_t *pos, void *o,
+                                 float *lse, int batch, int heads, int kv_heads, int d, int w, int g, float scale,
+                                 float sink_bias, bool bf16, hipStream_t stream);
+size_t decode_scratch_bytes();
 // keys per prefill tile (prefill.hip)
 constexpr int kPrefillBK = 64;
 inline int prefill_bq(bool bf16) { return prefill_rows_per_workgroup(bf16); }
@@ -70,6 +74,7 @@ const char *swa_strerror(int status) {
         case SWA_EALIGN: return "pointer not aligned (tensors need 16 bytes, lse 4 bytes)";
         case SWA_EHIP: return "the HIP runtime rejected a launch";
         case SWA_EWORKSPACE: return "decode workspace missing or too small";
+        case SWA_ESCRATCH: return "the shape needs more than the library's fixed decode scratch";
         default: return "unknown status";
     }
 }
@@ -320,6 +325,30 @@ int swa_decode_fwd_gqa(const void *q, const void *k_cache, const void *v_cache, 
     return status_of(swa::launch_decode(q, k_cache, v_cache, pos, o, lse, batch, heads, kv_heads, d, w, g, scale,
                                         sink_bias, dtype == SWA_BF16, workspace, stream));
 }
+
+int swa_decode_fwd_gqa_noalloc(const void *q, const void *k_cache, const void *v_cache, const int64_t *pos, void *o,
+                               float *lse, int batch, int heads, int kv_heads, int d, int w, int g, float scale,
+                               float sink_bias, swa_dtype_t dtype, hipStream_t stream) {
+    if (!q || !k_cache || !v_cache || !pos || !o) return SWA_EINVAL;
+    if (batch < 1 || heads < 1 || w < 1 || g < 0) return SWA_EINVAL;
+    if (kv_heads < 1 || kv_heads > heads || heads % kv_heads != 0) return SWA_EINVAL;
+    if ((long long)g + w > INT_MAX / 2) return SWA_EINVAL;
+    if ((long long)batch * heads > INT_MAX / 64) return SWA_EINVAL;
+    if (((long long)g + w) * d * 4 >= (1LL << 32)) return SWA_EINVAL;
+    if (!std::isfinite(scale) || !(scale > 0.f) || !std::isfinite(sink_bias)) return SWA_EINVAL;
+    int st = check_dtype_d(dtype, d);
+    if (st != SWA_OK) return st;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+        (reinterpret_cast<uintptr_t>(pos) & 7u) || (lse && !aligned4(lse)))
+        return SWA_EALIGN;
+    const size_t need = swa::decode_workspace_bytes(batch, heads, kv_heads, d, g + w,
+                                                    swa::decode_kind(dtype == SWA_BF16, false, heads, kv_heads));
+    if (need > swa::decode_scratch_bytes()) return SWA_ESCRATCH;
+    return status_of(swa::launch_decode_noalloc(q, k_cache, v_cache, pos, o, lse, batch, heads, kv_heads, d, w, g,
+                                                scale, sink_bias, dtype == SWA_BF16, stream));
+}
+
+size_t swa_decode_scratch_bytes(void) { return swa::decode_scratch_bytes(); }
 
 int swa_decode_fwd(const void *q, const void *k_cache, const void *v_cache, const int64_t *pos, void *o, float *lse,
                    int batch, int heads, int d, int w, int g, float scale, float sink_bias, swa_dtype_t dtype,

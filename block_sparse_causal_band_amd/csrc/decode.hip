@@ -26,6 +26,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -986,6 +987,64 @@ hipError_t launch_kv_append_fp8(void *kc, void *vc, const void *kn, const void *
         hipLaunchKernelGGL(kv_append_fp8_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, (uint8_t *)kc,
                            (uint8_t *)vc, kn, vn, pos, ksc, vsc, heads, tn, d, w, g, total);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fixed device scratch for the decode entry point that allocates nothing: the
+// split decode's partial (m, l, o) records go here instead of into a
+// caller-supplied workspace.  Every device the library runs on holds its own
+// copy until the process ends; calls that overlap on one device share it and
+// race.  The kernels overwrite every record they later read, so nothing in it
+// needs clearing between calls.
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+size_t decode_scratch_bytes() { return kDecodeScratchBytes; }
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+// Device address of `scratch` on the device that owns `stream`, looked up once
+// per device with that device current (the host-side name of the array is
+// only a stand-in and is never passed to a kernel).
+static hipError_t decode_scratch_address(hipStream_t stream, void **out) {
+    int dev = -1;
+    hipError_t e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        int cur = -1;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+// launch_decode with the partial records in the fixed scratch (the caller has
+// checked that the launch needs at most kDecodeScratchBytes).
+hipError_t launch_decode_noalloc(const void *q, const void *kc, const void *vc, const int64_t *pos, void *o,
+                                 float *lse, int batch, int heads, int kv_heads, int d, int w, int g, float scale,
+                                 float sink_bias, bool bf16, hipStream_t stream) {
+    void *ws = nullptr;
+    const hipError_t e = decode_scratch_address(stream, &ws);
+    if (e != hipSuccess) return e;
+    return launch_decode(q, kc, vc, pos, o, lse, batch, heads, kv_heads, d, w, g, scale, sink_bias, bf16, ws,
+                         stream);
 }
 
 }  // namespace swa

@@ -26,7 +26,8 @@
  *
  * Conventions for every entry point
  *  - Tensor pointers are DEVICE pointers owned by the caller; the library
- *    allocates nothing and keeps no state between calls.  Every tensor is
+ *    allocates nothing and keeps no state between calls, except the fixed
+ *    decode scratch of swa_decode_fwd_gqa_noalloc below.  Every tensor is
  *    contiguous with the innermost dimension last, as written below, and
  *    every pointer must be 16-byte aligned.
  *  - Work is enqueued asynchronously on `stream` (0 = the null stream); the
@@ -61,7 +62,8 @@ enum {
     SWA_EUNSUPPORTED = -2,  /* head dimension or dtype not supported            */
     SWA_EALIGN = -3,        /* a pointer is not 16-byte aligned                 */
     SWA_EHIP = -4,          /* the HIP runtime rejected a launch                */
-    SWA_EWORKSPACE = -5     /* decode workspace missing or too small            */
+    SWA_EWORKSPACE = -5,    /* decode workspace missing or too small            */
+    SWA_ESCRATCH = -6       /* shape needs more than the fixed decode scratch   */
 };
 
 /*
@@ -152,6 +154,30 @@ int swa_decode_fwd_gqa(const void *q, const void *k_cache, const void *v_cache, 
                        void *workspace, size_t workspace_bytes, hipStream_t stream);
 /* Workspace bytes of swa_decode_fwd_gqa (0 also for an invalid shape). */
 size_t swa_decode_workspace_bytes_gqa(int batch, int heads, int kv_heads, int d, int w, int g);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation, kernels and results as swa_decode_fwd_gqa, with no workspace
+ * argument.  When the launch splits the cache rows of one (batch, head)
+ * across workgroups, the partial (m, l, o) records go to a fixed scratch
+ * array of swa_decode_scratch_bytes() bytes (16 MiB) that the library keeps
+ * in device memory, one copy per device, from the first call on that device
+ * until the process ends.  The call itself allocates nothing: its first call
+ * on a device only looks up that device's copy (hipGetSymbolAddress).
+ * Calls that overlap in time on one device (different streams, or host
+ * threads) share the array and race; calls ordered on one stream do not.
+ * Every record a call reads was written by that call's own first kernel, so
+ * nothing needs clearing between calls.  Arguments, layout, ownership and
+ * errors as swa_decode_fwd_gqa, plus SWA_ESCRATCH when the shape's partial
+ * records (swa_decode_workspace_bytes_gqa) would exceed the array; by the
+ * split rule in use no shape reaches 13 MiB, so this is a guard, not a
+ * limit callers meet.
+ */
+int swa_decode_fwd_gqa_noalloc(const void *q, const void *k_cache, const void *v_cache, const int64_t *pos,
+                               void *o, float *lse, int batch, int heads, int kv_heads, int d, int w, int g,
+                               float scale, float sink_bias, swa_dtype_t dtype, hipStream_t stream);
+size_t swa_decode_scratch_bytes(void);
 
 /*
  * Chunked prefill against the rolling cache: t new tokens of each batch entry

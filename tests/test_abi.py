@@ -12,7 +12,7 @@ from block_sparse_causal_band_amd import binding
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "swa.h")
 
-OK, EINVAL, EUNSUP, EALIGN, EHIP, EWS = 0, -1, -2, -3, -4, -5
+OK, EINVAL, EUNSUP, EALIGN, EHIP, EWS, ESCRATCH = 0, -1, -2, -3, -4, -5, -6
 P = 4096  # a fake, 16-byte aligned "device pointer": never dereferenced on these paths
 
 
@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_strerror_covers_every_status():
-    for st in (OK, EINVAL, EUNSUP, EALIGN, EHIP, EWS):
+    for st in (OK, EINVAL, EUNSUP, EALIGN, EHIP, EWS, ESCRATCH):
         assert swa.strerror(st) and swa.strerror(st) != "unknown status"
     assert swa.strerror(-99) == "unknown status"
 
@@ -104,6 +104,47 @@ def test_decode_workspace_sizes():
     need = swa.decode_workspace_bytes(1, 1, 128, 4096, 4)
     assert need > 0 and need % 16 == 0
     assert swa.decode_workspace_bytes(1, 1, 96, 4096, 4) == 0           # unsupported d: nothing to size
+
+
+def _decode_noalloc(**kw):
+    a = dict(q=P, kc=P, vc=P, pos=P, o=P, lse=None, batch=64, heads=32, kv_heads=8, d=128, w=4096, g=4,
+             scale=0.125, bias=0.0, dtype=1)
+    a.update(kw)
+    return swa.lib().swa_decode_fwd_gqa_noalloc(a["q"], a["kc"], a["vc"], a["pos"], a["o"], a["lse"], a["batch"],
+                                                a["heads"], a["kv_heads"], a["d"], a["w"], a["g"], a["scale"],
+                                                a["bias"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), EINVAL), (dict(kc=None), EINVAL), (dict(vc=None), EINVAL), (dict(pos=None), EINVAL),
+    (dict(o=None), EINVAL), (dict(batch=0), EINVAL), (dict(heads=0), EINVAL), (dict(kv_heads=3), EINVAL),
+    (dict(w=0), EINVAL), (dict(g=-1), EINVAL), (dict(scale=0.0), EINVAL), (dict(bias=float("inf")), EINVAL),
+    (dict(w=2**31 - 8), EINVAL), (dict(d=80), EUNSUP), (dict(dtype=2), EUNSUP),
+    (dict(q=P + 8), EALIGN), (dict(pos=P + 4), EALIGN), (dict(lse=P + 2), EALIGN),
+])
+def test_decode_noalloc_rejects(kw, want):
+    assert _decode_noalloc(**kw) == want
+
+
+def test_decode_scratch_covers_every_split():
+    """The fixed scratch of the allocation-free decode holds the partial
+    records of every shape the split rule can produce: the records peak just
+    below the job counts at which a launch stops splitting, so sweep those
+    (and a coarse grid) over every group size, both head dims and short and
+    long caches; the workspace size here is the largest any kernel needs."""
+    L = swa.lib()
+    cap = int(L.swa_decode_scratch_bytes())
+    assert cap == 16 << 20
+    worst = 0
+    for d in (64, 128):
+        for group in (1, 2, 3, 4, 8, 16, 32):
+            for kvh in list(range(1, 80)) + [127, 128, 255, 256, 511, 512, 1023, 1024, 2047]:
+                heads = kvh * group
+                for rows in (256, 1028, 4100, 65540):
+                    need = int(L.swa_decode_workspace_bytes_gqa(1, heads, kvh, d, rows - 4, 4))
+                    worst = max(worst, need)
+                    assert need <= cap, (d, group, heads, rows, need)
+    assert worst > (1 << 20)  # the sweep reaches the large splits
 
 
 def _prefill_gqa(**kw):
