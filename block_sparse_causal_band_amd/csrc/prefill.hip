@@ -541,8 +541,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     scores(kbuf0, s_cur);
     __syncthreads();  // every wave is done with K(0) before K(2) replaces it
 
-    auto do_tile_p = [&](int t, auto masked_tag, auto par_tag) __attribute__((always_inline)) {
+    auto do_tile_p = [&](int t, auto masked_tag, auto par_tag, auto last_tag) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_tag)::value;
+        constexpr bool LAST = decltype(last_tag)::value;  // the block's last tile: no next tile to score
         constexpr int PAR = decltype(par_tag)::value;  // t & 1, or 2: from t at run time
         const int par = (PAR == 2) ? (t & 1) : PAR;
         uint8_t *const kcur = par ? kbuf1 : kbuf0;
@@ -576,8 +577,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
         // Every K fragment of tile t+1 is read at the top of the tile (on cut
         // tiles the mask and the row max of tile t then cover the latency).
         bf16x8 kf[NS];
+        if constexpr (!LAST) {
 #pragma unroll
-        for (int j = 0; j < NS; ++j) kf[j] = kfrag(j);
+            for (int j = 0; j < NS; ++j) kf[j] = kfrag(j);
+        }
 
         if constexpr (MASKED) {
             mask_tile<CHUNK || STRIDED>(s_cur, qa, k0, lh, khi, wq, g, bias_raw, klo);
@@ -593,8 +596,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
         //     dot2s; the first V^T fragments of B are read during its last
         //     MFMAs;
         //  B: the PV MFMAs of tile t (V^T fragments read 3 MFMAs ahead).
-        // On the last tile the A stream reads the other K buffer and its
-        // result is discarded.  The whole stretch runs at raised wave
+        // The last tile has no next tile: its A stream is the exponentials
+        // alone.  The whole stretch runs at raised wave
         // priority, so when both waves of a SIMD are ready the one feeding
         // the matrix core issues first.
         __builtin_amdgcn_s_setprio(1);
@@ -621,7 +624,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
             if (j >= NS - VA) vf[j - (NS - VA)] = vfrag(j - (NS - VA));
-            s_nxt[j / NC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j], qf[j % NC], s_nxt[j / NC], 0, 0, 0);
+            if constexpr (!LAST)
+                s_nxt[j / NC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j], qf[j % NC], s_nxt[j / NC], 0, 0, 0);
 #pragma unroll
             for (int q = 0; q < EPS / 2; ++q) prob_pair((EPS / 2) * j + q);
             __builtin_amdgcn_sched_barrier(0);
@@ -656,8 +660,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
             }
         }
         l_run += ls0 + ls1;
-        s_cur[0] = s_nxt[0];
-        s_cur[1] = s_nxt[1];
+        if constexpr (!LAST) {
+            s_cur[0] = s_nxt[0];
+            s_cur[1] = s_nxt[1];
+        }
         __builtin_amdgcn_s_setprio(0);
 
         __builtin_amdgcn_s_waitcnt(0);  // K(t+2) and V(t+1) of this wave have landed
@@ -669,27 +675,42 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     int t_lo = 0, t_hi = ntiles;  // a wave entirely past n keeps all tiles unmasked (nothing is stored)
     const int qw0 = q0 + wave * 32;
     if (qw0 < nq) full_range(band, qpos(qw0), qpos(min(qw0 + 31, nq - 1)), khi, wq, g, kBK, &t_lo, &t_hi, klo);
+    // The last tile runs on its own (no next tile to score) and with the
+    // mask, which leaves a FULL tile's scores as they are.  (The chunk
+    // kernel keeps the discarded score stream on its last tile: a separate
+    // last-tile body does not fit its registers without a spill.)
+    if constexpr (!CHUNK) {
+        if (t_hi > ntiles - 1) t_hi = ntiles - 1;
+        if (t_lo > t_hi) t_lo = t_hi;
+    }
     // The FULL run is unrolled by two so that each tile body names its
     // buffers statically (parity 0 / 1); the cut tiles take the parity at run
     // time (2).
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
     using P2 = std::integral_constant<int, 2>;
+    using T = std::true_type;
+    using F = std::false_type;
     int t = 0;
-    for (; t < t_lo; ++t) do_tile_p(t, std::true_type{}, P2{});
+    for (; t < t_lo; ++t) do_tile_p(t, T{}, P2{}, F{});
     if ((t & 1) && t < t_hi) {
-        do_tile_p(t, std::false_type{}, P1{});
+        do_tile_p(t, F{}, P1{}, F{});
         ++t;
     }
     for (; t + 1 < t_hi; t += 2) {
-        do_tile_p(t, std::false_type{}, P0{});
-        do_tile_p(t + 1, std::false_type{}, P1{});
+        do_tile_p(t, F{}, P0{}, F{});
+        do_tile_p(t + 1, F{}, P1{}, F{});
     }
     if (t < t_hi) {
-        do_tile_p(t, std::false_type{}, P0{});
+        do_tile_p(t, F{}, P0{}, F{});
         ++t;
     }
-    for (; t < ntiles; ++t) do_tile_p(t, std::true_type{}, P2{});
+    if constexpr (CHUNK) {
+        for (; t < ntiles; ++t) do_tile_p(t, T{}, P2{}, F{});
+    } else {
+        for (; t < ntiles - 1; ++t) do_tile_p(t, T{}, P2{}, F{});
+        do_tile_p(ntiles - 1, T{}, P2{}, T{});
+    }
 
     // the loop's last barrier has every wave past its LDS reads; each wave
     // stages its rows in its own 32 * 2D bytes of the K buffers
