@@ -1,26 +1,39 @@
 #!/usr/bin/env python3
 """Throughput of exact causal sliding-window attention (+ sinks) on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-extras] [--no-cold] [--no-cpu-baseline]
 
-Prints ONE JSON line.  The default workload is the Mistral-7B-shaped prefill
-(batch 1, 32 heads, n=16384, d=128, w=4096, bf16): one step = one prefill
-launch over the whole prompt, inputs already resident in HBM.  `value` is
-band-TFLOP/s: 4*d FLOP per attended (query, key) pair (two products, a
-multiply-add counted as 2), attended pairs counted exactly per row.  The
-same line carries the rolling-cache decode workload (batch 64, 32 heads,
-d=128, w=4096, g=4, positions in [4096, 131072]) as KV GB/s: bytes of the
-key/value rows each query attends, plus q and o.
+Prints ONE JSON line.  The headline workload is the sink prefill: batch 1,
+32 heads, n=32768, d=128, w=4096, g=4 sink tokens with a +4 logit offset,
+bf16.  One step = one prefill launch over the whole prompt, inputs already
+resident in HBM.  `value` is band-TFLOP/s: 4*d FLOP per attended (query,
+key) pair (two products, a multiply-add counted as 2), pairs counted exactly
+per row.
 
-`roofline` is for the dominant kernel of the line's workload, timed with
-events on the stream the kernel runs on.  `cpu_baseline` is the fp64 oracle
-on a bounded sample of the same workload, on the host's cores.
+The same line carries, under "extra", the Mistral-shaped prefill (n=16384,
+w=4096), the Gemma-3-style local prefill (16 heads, n=131072, w=1024), the
+rolling-cache decode (batch 64, 32 heads, w=4096, g=4, positions in [4096,
+131072]; KV GB/s) and that decode step's one-token kv_append, each with its
+own roofline.  They run before the headline, which is timed last.
+
+Timing: every launch is bracketed by HIP events on the stream the kernel
+runs on; `ms_per_step` is the whole timed region over K steps, `roofline`
+gives the mean, median, p10 and p90 launch times.  For prefill a cold-cache
+figure follows: a 1 GiB scratch write between launches evicts L2 and MALL
+before each timed launch.
+
+`roofline.traffic` is HBM bytes per launch from rocprofv3 FETCH_SIZE and
+WRITE_SIZE (calibrated on a plain device copy), reported only while the
+kernel sources match the ones the counters were taken on; `roofline.counters`
+likewise carries the matrix-core figures of the same profiles.
+`cpu_baseline` is the fp64 oracle on a bounded sample of the headline
+workload, on all the host's cores and on one core.
 """
 from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -33,6 +46,7 @@ METRIC = "SWA prefill band-TFLOP/s and decode KV GB/s, % of MI355X peak, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (matrix and vector)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+HEADLINE = "sink_prefill"
 
 PREFILL = {
     # name: (batch, heads, n, d, w, g, sink_bias, seed)
@@ -40,6 +54,11 @@ PREFILL = {
     "mistral_prefill": (1, 32, 16384, 128, 4096, 0, 0.0, 2),
     "sink_prefill": (1, 32, 32768, 128, 4096, 4, 4.0, 3),
     "gemma3_local_prefill": (1, 16, 131072, 128, 1024, 0, 0.0, 5),
+}
+# grouped-query prefill: (batch, heads, kv_heads, n, d, w, g, sink_bias, seed);
+# Mistral 7B's 32 query heads over 8 key/value heads
+PREFILL_GQA = {
+    "gqa_prefill": (1, 32, 8, 16384, 128, 4096, 0, 0.0, 9),
 }
 DECODE = {
     # name: (batch, heads, kv_heads, d, w, g, pos_lo, pos_hi, seed)
@@ -72,14 +91,18 @@ PATTERN = {
 # the source has changed since, the figure no longer describes the kernel and
 # `traffic` is reported as null.
 MEASURED_TRAFFIC = {
-    "mistral_prefill": {"bytes": 537654927, "source_digest": "f4050d4cfde5a500"},
-    "sink_prefill": {"bytes": 1074220565, "source_digest": "f4050d4cfde5a500"},
-    "gemma3_local_prefill": {"bytes": 2226296863, "source_digest": "f4050d4cfde5a500"},
-    "chunk_prefill": {"bytes": 140024216, "source_digest": "f4050d4cfde5a500"},
     "rolling_decode": {"bytes": 4300265431, "source_digest": "1197048432c9c06b"},
     "gqa_decode": {"bytes": 1076057369, "source_digest": "1197048432c9c06b"},
     "fp8_decode": {"bytes": 2151013950, "source_digest": "1197048432c9c06b"},
 }
+# Matrix-core figures of the prefill kernels from rocprofv3 counter runs
+# (SQ_INSTS_MFMA, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, SQ_BUSY_CYCLES per
+# dispatch), keyed by workload, with the digest of the sources they were
+# taken on (reported as null once the kernel has changed):
+#   issued_per_band: MFMA FLOP issued (SQ_INSTS_MFMA x 32768) / band FLOP;
+#   mfma_busy_per_simd: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs);
+#   clock_ghz: GRBM_GUI_ACTIVE / 8 XCDs / kernel duration.
+MEASURED_COUNTERS: dict = {}
 CSRC = os.path.join(ROOT, "block_sparse_causal_band_amd", "csrc")
 
 
@@ -97,11 +120,21 @@ def kernel_source_digest(name: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, source: str):
-    entry = MEASURED_TRAFFIC.get(workload)
+def _measured(table, workload: str, source: str):
+    entry = table.get(workload)
     if entry is None or entry["source_digest"] != kernel_source_digest(source):
         return None
-    return entry["bytes"]
+    return entry
+
+
+def measured_traffic(workload: str, source: str):
+    entry = _measured(MEASURED_TRAFFIC, workload, source)
+    return None if entry is None else entry["bytes"]
+
+
+def measured_counters(workload: str):
+    entry = _measured(MEASURED_COUNTERS, workload, "prefill.hip")
+    return None if entry is None else {k: v for k, v in entry.items() if k != "source_digest"}
 
 
 def row_pairs(i: int, w: int, g: int) -> int:
@@ -122,7 +155,25 @@ def band_pairs(n: int, w: int, g: int) -> int:
     return pairs
 
 
-def _events_time(fn, steps, stream):
+def _pct(xs, q):
+    xs = sorted(xs)
+    if not xs:
+        return None
+    pos = (len(xs) - 1) * q
+    lo = int(pos)
+    hi = min(lo + 1, len(xs) - 1)
+    return xs[lo] + (xs[hi] - xs[lo]) * (pos - lo)
+
+
+def _stats(per):
+    return {"mean": sum(per) / len(per), "median": _pct(per, 0.5), "p10": _pct(per, 0.1), "p90": _pct(per, 0.9),
+            "min": min(per), "max": max(per), "launches": len(per)}
+
+
+def _events_time(fn, steps, stream, between=None):
+    """Times `steps` calls of fn, each bracketed by events on `stream`.
+    Returns (elapsed ms of the whole region / steps, per-call ms list).
+    `between` (untimed, on the same stream) runs before each call."""
     import torch
 
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -131,17 +182,36 @@ def _events_time(fn, steps, stream):
     torch.cuda.synchronize()
     t0.record(stream)
     for a, b in evs:
+        if between is not None:
+            between()
         a.record(stream)
         fn()
         b.record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     per = [a.elapsed_time(b) for a, b in evs]
-    total = t0.elapsed_time(t1)
-    return total / steps, sum(per) / len(per), per
+    return t0.elapsed_time(t1) / steps, per
 
 
-def bench_prefill(name, steps, warmup):
+def _run(step, steps, warmup):
+    import torch
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    return _events_time(step, steps, torch.cuda.current_stream())
+
+
+def _roofline(bound, work, per, peak, unit, traffic, kernel, counters=None):
+    st = _stats(per)
+    achieved = work / (st["mean"] * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+    return {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+            "traffic": traffic, "kernel": kernel, "launch_ms": st,
+            "frac_median": work / (st["median"] * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9) / peak,
+            "counters": counters}
+
+
+def bench_prefill(name, steps, warmup, cold=False):
     import torch
 
     import block_sparse_causal_band_amd as swa
@@ -152,20 +222,14 @@ def bench_prefill(name, steps, warmup):
     dev = torch.device("cuda")
     q, k, v = synth.qkv(B, H, n, d, dtype, seed=seed, device=dev)
     o = torch.empty_like(q)
-    stream = torch.cuda.current_stream()
 
     def step():
         swa.prefill(q, k, v, w=w, g=g, sink_bias=beta, out=o)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    ms_step, ms_launch, per = _events_time(step, steps, stream)
+    ms_step, per = _run(step, steps, warmup)
     flops = 4.0 * d * band_pairs(n, w, g) * B * H
     peak = PEAK_BF16_TFLOPS if dtype == torch.bfloat16 else PEAK_F32_TFLOPS
-    achieved = flops / (ms_launch * 1e-3) / 1e12
-    traffic = measured_traffic(name, "prefill.hip")
-    return {
+    r = {
         "ms_per_step": ms_step,
         "value": flops / (ms_step * 1e-3) / 1e12,
         "unit": "TFLOP/s",
@@ -173,10 +237,62 @@ def bench_prefill(name, steps, warmup):
         "config": {"workload": name, "batch": B, "heads": H, "n": n, "d": d, "w": w, "g": g,
                    "sink_bias": beta, "band_flops_per_step": flops,
                    "page_formula_flops_4nwd": 4.0 * n * w * d * B * H},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": traffic,
-                     "kernel": f"prefill_bf16_kernel<{d},4>" if dtype == torch.bfloat16 else f"prefill_f32_kernel<{d}>",
-                     "avg_launch_ms": ms_launch, "min_launch_ms": min(per)},
+        "roofline": _roofline("mfma", flops, per, peak, "TFLOP/s", measured_traffic(name, "prefill.hip"),
+                              f"prefill_bf16_kernel<{d}>" if dtype == torch.bfloat16 else f"prefill_f32_kernel<{d}>",
+                              measured_counters(name)),
+    }
+    if cold:
+        r["cold_cache"] = _cold(step, flops, peak, steps)
+    del q, k, v, o
+    return r
+
+
+def _cold(step, flops, peak, steps):
+    """Launches timed after a 1 GiB scratch write (L2 and MALL hold none of the inputs)."""
+    import torch
+
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    val = [0]
+
+    def flush():
+        val[0] = (val[0] + 1) & 0xFF
+        scratch.fill_(val[0])
+
+    flush()
+    torch.cuda.synchronize()
+    _, per = _events_time(step, min(steps, 20), torch.cuda.current_stream(), between=flush)
+    st = _stats(per)
+    del scratch
+    return {"launch_ms": st, "value_median": flops / (st["median"] * 1e-3) / 1e12, "unit": "TFLOP/s",
+            "frac_median": flops / (st["median"] * 1e-3) / 1e12 / peak,
+            "note": "1 GiB scratch written before each timed launch"}
+
+
+def bench_prefill_gqa(name, steps, warmup):
+    import torch
+
+    import block_sparse_causal_band_amd as swa
+    from block_sparse_causal_band_amd import synth
+
+    B, H, Hkv, n, d, w, g, beta, seed = PREFILL_GQA[name]
+    dev = torch.device("cuda")
+    q, k, v = synth.qkv(B, H, n, d, torch.bfloat16, seed=seed, device=dev, kv_heads=Hkv)
+    o = torch.empty_like(q)
+
+    def step():
+        swa.prefill(q, k, v, w=w, g=g, sink_bias=beta, out=o)
+
+    ms_step, per = _run(step, steps, warmup)
+    flops = 4.0 * d * band_pairs(n, w, g) * B * H
+    return {
+        "ms_per_step": ms_step,
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "dtype": "bf16",
+        "config": {"workload": name, "batch": B, "heads": H, "kv_heads": Hkv, "n": n, "d": d, "w": w, "g": g,
+                   "sink_bias": beta, "band_flops_per_step": flops},
+        "roofline": _roofline("mfma", flops, per, PEAK_BF16_TFLOPS, "TFLOP/s", measured_traffic(name, "prefill.hip"),
+                              f"prefill_bf16_kernel<{d}> (grouped query heads)", measured_counters(name)),
     }
 
 
@@ -197,17 +313,12 @@ def bench_chunk(name, steps, warmup):
     vc = synth.normal((B, Hkv, g + w, d), seed=seed + 2, dtype=torch.bfloat16, device=dev)
     pos = torch.full((B,), p0, dtype=torch.int64, device=dev)
     o = torch.empty_like(q)
-    stream = torch.cuda.current_stream()
 
     def step():
         swa.chunk_prefill(q, kn, vn, kc, vc, pos, w=w, g=g, sink_bias=beta, out=o)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    ms_step, ms_launch, per = _events_time(step, steps, stream)
+    ms_step, per = _run(step, steps, warmup)
     flops = 4.0 * d * chunk_pairs(p0, T, w, g) * B * H
-    achieved = flops / (ms_launch * 1e-3) / 1e12
     return {
         "ms_per_step": ms_step,
         "value": flops / (ms_step * 1e-3) / 1e12,
@@ -215,42 +326,9 @@ def bench_chunk(name, steps, warmup):
         "dtype": "bf16",
         "config": {"workload": name, "batch": B, "heads": H, "kv_heads": Hkv, "t": T, "p0": p0, "d": d, "w": w,
                    "g": g, "sink_bias": beta, "band_flops_per_step": flops},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(name, "prefill.hip"),
-                     "kernel": f"prefill_bf16_kernel<{d},4,chunk>",
-                     "avg_launch_ms": ms_launch, "min_launch_ms": min(per)},
+        "roofline": _roofline("mfma", flops, per, PEAK_BF16_TFLOPS, "TFLOP/s", measured_traffic(name, "prefill.hip"),
+                              f"prefill_bf16_kernel<{d},chunk>", measured_counters(name)),
     }
-
-
-def cpu_baseline_chunk(name, budget_s=12.0):
-    """The fp64 oracle on chunk rows of the same workload (each row given the
-    window and sink rows it attends), until about budget_s seconds."""
-    import numpy as np
-    import torch
-
-    import oracle
-    from block_sparse_causal_band_amd import synth
-
-    B, H, Hkv, T, p0, d, w, g, beta, seed = CHUNK[name]
-    orc = oracle.default()
-    units = 32
-    nk = w + g
-    q = synth.normal((units, d), seed=seed, dtype=torch.bfloat16)
-    kk = synth.normal((units, nk, d), seed=seed + 1, dtype=torch.bfloat16)
-    vv = synth.normal((units, nk, d), seed=seed + 2, dtype=torch.bfloat16)
-    rng = np.random.default_rng(seed)
-    done_pairs, done = 0, 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
-        ps = p0 + rng.integers(0, T, units)
-        kpos = np.stack([np.concatenate([np.arange(p - w + 1, p + 1), np.arange(0, min(g, p - w + 1))]) for p in ps])
-        orc.decode(q, ps, kpos, kk, vv, w=w, g=g, beta=beta)
-        done_pairs += sum(row_pairs(int(p), w, g) for p in ps)
-        done += units
-    dt = time.perf_counter() - t0
-    return {"value": 4.0 * d * done_pairs / dt / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(),
-            "kind": "oracle", "sample": f"{done} chunk rows of {name} (random rows, each with its {nk} attended keys), "
-                                        f"fp64, {dt:.1f} s"}
 
 
 def pattern_pairs(n: int, kind: str, w: int, g: int, r: int) -> int:
@@ -277,7 +355,6 @@ def bench_pattern(name, steps, warmup):
     q, k, v = synth.qkv(B, H, n, d, torch.bfloat16, seed=seed, device=dev)
     o = torch.empty_like(q)
     ws = torch.empty(max(swa.landmark_workspace_bytes(B, H, n, d, swa.SWA_BF16), 16), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
 
     def step():
         if kind == "dilated":
@@ -285,12 +362,8 @@ def bench_pattern(name, steps, warmup):
         else:
             swa.landmark_prefill(q, k, v, w=w, g=g, r=r, sink_bias=beta, out=o, workspace=ws)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    ms_step, ms_launch, per = _events_time(step, steps, stream)
+    ms_step, per = _run(step, steps, warmup)
     flops = 4.0 * d * pattern_pairs(n, kind, w, g, r) * B * H
-    achieved = flops / (ms_launch * 1e-3) / 1e12
     return {
         "ms_per_step": ms_step,
         "value": flops / (ms_step * 1e-3) / 1e12,
@@ -298,38 +371,10 @@ def bench_pattern(name, steps, warmup):
         "dtype": "bf16",
         "config": {"workload": name, "batch": B, "heads": H, "n": n, "d": d, "pattern": kind, "w": w, "g": g,
                    "r": r, "sink_bias": beta, "band_flops_per_step": flops},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                     "kernel": ("prefill_bf16_kernel<128,4,strided> (dilated classes)" if kind == "dilated" else
-                                "window prefill + landmark part merged in its epilogue (one call)"),
-                     "avg_launch_ms": ms_launch, "min_launch_ms": min(per)},
+        "roofline": _roofline("mfma", flops, per, PEAK_BF16_TFLOPS, "TFLOP/s", None,
+                              ("prefill_bf16_kernel<128,strided> (dilated classes)" if kind == "dilated" else
+                               "window prefill + landmark part merged in its epilogue (one call, two launches)")),
     }
-
-
-def cpu_baseline_pattern(name, budget_s=12.0):
-    """The oracle's pattern rows (oracle/patterns.py, fp64 numpy) on the last
-    rows of one head of the same workload, until about budget_s seconds."""
-    import numpy as np
-    import torch
-
-    from block_sparse_causal_band_amd import synth
-    from oracle import patterns
-
-    B, H, n, d, kind, w, g, r, beta, seed = PATTERN[name]
-    q, k, v = synth.qkv(1, 1, n, d, torch.bfloat16, seed=seed, device="cpu")
-    qh, kh, vh = (t[0, 0].double().numpy() for t in (q, k, v))
-    done_pairs, done, t0 = 0, 0, time.perf_counter()
-    i = n - 1
-    while time.perf_counter() - t0 < budget_s and i >= 0:
-        rows = np.arange(max(0, i - 63), i + 1)
-        patterns.prefill(qh, kh, vh, kind, w=w, g=g, r=r, beta=beta, rows=rows)
-        for j in rows:
-            done_pairs += len(patterns.read_set(int(j), kind, w, g, r))
-        done += len(rows)
-        i -= 64
-    dt = time.perf_counter() - t0
-    return {"value": 4.0 * d * done_pairs / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} rows of one head of {name} (from the last row back), fp64 numpy, {dt:.1f} s"}
 
 
 def bench_decode(name, steps, warmup):
@@ -350,7 +395,6 @@ def bench_decode(name, steps, warmup):
     o = torch.empty_like(q)
     ws_bytes = swa.decode_workspace_bytes(B, H, d, w, g, kv_heads=Hkv)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
 
     def step():
         if fp8:
@@ -358,34 +402,68 @@ def bench_decode(name, steps, warmup):
         else:
             swa.decode(q, kc, vc, pos, w=w, g=g, out=o, workspace=ws)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    ms_step, ms_launch, per = _events_time(step, steps, stream)
+    ms_step, per = _run(step, steps, warmup)
     # algorithmic bytes: each (batch, key/value head)'s attended K and V rows
     # once (shared by the query heads of its group), plus q and o
     rows = sum(row_pairs(int(p), w, g) for p in pos.cpu().tolist()) * Hkv
     nbytes = rows * d * (1 if fp8 else 2) * 2 + 2 * B * H * d * 2
-    achieved = nbytes / (ms_launch * 1e-3) / 1e9
-    traffic = measured_traffic(name, "decode.hip")
-    return {
+    r = {
         "ms_per_step": ms_step,
         "value": nbytes / (ms_step * 1e-3) / 1e9,
         "unit": "GB/s",
-        "dtype": "bf16",
+        "dtype": "fp8_e4m3 cache, bf16 q/o, fp32 arithmetic" if fp8 else "bf16",
         "config": {"workload": name, "batch": B, "heads": H, "kv_heads": Hkv, "d": d, "w": w, "g": g,
                    "positions": [lo, hi], "kv_bytes_per_step": nbytes},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel": ("decode_kernel<bf16,fp8x16,128>" if fp8 else
-                                "decode_mfma_kernel<128>" if Hkv < H else "decode_kernel<bf16,bf16,128>"),
-                     "avg_launch_ms": ms_launch, "min_launch_ms": min(per)},
+        "roofline": _roofline("hbm", nbytes, per, PEAK_HBM_GBS, "GB/s", measured_traffic(name, "decode.hip"),
+                              ("decode_kernel<bf16,fp8x16,128>" if fp8 else
+                               "decode_mfma_kernel<128>" if Hkv < H else "decode_kernel<bf16,bf16,128>")),
     }
+    del q, kc, vc, o
+    return r
 
 
-def cpu_baseline_prefill(name, budget_s=12.0):
+def bench_kv_append(name, steps, warmup):
+    """The decode step's append: one new token per (batch, key/value head)
+    written to its ring row (and sink row below g)."""
+    import torch
+
+    import block_sparse_causal_band_amd as swa
+    from block_sparse_causal_band_amd import synth
+
+    B, H, Hkv, d, w, g, lo, hi, seed = DECODE[name]
+    dev = torch.device("cuda")
+    _, kc, vc, pos = synth.decode_problem(B, H, d, g + w, lo, hi, torch.bfloat16, seed=seed, device=dev,
+                                          kv_heads=Hkv)
+    kn = synth.normal((B, Hkv, 1, d), seed=seed + 7, dtype=torch.bfloat16, device=dev)
+    vn = synth.normal((B, Hkv, 1, d), seed=seed + 8, dtype=torch.bfloat16, device=dev)
+
+    def step():
+        swa.kv_append(kc, vc, kn, vn, pos, w=w, g=g)
+
+    ms_step, per = _run(step, steps, warmup)
+    writes = sum(2 if int(p) < g else 1 for p in pos.cpu().tolist()) * Hkv
+    nbytes = 2 * B * Hkv * d * 2 + writes * 2 * d * 2  # k_new, v_new read; cache rows written
+    return {"ms_per_step": ms_step, "value": nbytes / (ms_step * 1e-3) / 1e9, "unit": "GB/s", "dtype": "bf16",
+            "config": {"workload": f"{name} append (1 token)", "batch": B, "kv_heads": Hkv, "d": d, "w": w, "g": g,
+                       "bytes_per_step": nbytes},
+            "roofline": _roofline("hbm", nbytes, per, PEAK_HBM_GBS, "GB/s", None, "kv_append_kernel<bf16>")}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline_prefill(name, budget_s=12.0, single_s=3.0):
     """The fp64 oracle, as it stands, on whole heads of the same workload until
-    about budget_s seconds of CPU work; rate in band-TFLOP/s."""
+    about budget_s seconds of CPU work on every core, then on one core for
+    about single_s seconds; rates in band-TFLOP/s."""
     import numpy as np
     import torch
 
@@ -396,33 +474,43 @@ def cpu_baseline_prefill(name, budget_s=12.0):
     dtype = torch.float32 if name == "tiny_fp32" else torch.bfloat16
     q, k, v = synth.qkv(B, H, n, d, dtype, seed=seed, device="cpu")
     orc = oracle.default()
+    threads = orc.num_threads()
     rows_per_chunk = 512 if n >= 4096 else n
-    done_pairs = 0
-    done_rows = 0
-    heads_touched = 0
-    t0 = time.perf_counter()
-    # whole heads, each from its last rows backwards (full-window rows are the
-    # bulk of the workload), until the budget is spent
-    for bh in range(B * H):
-        if time.perf_counter() - t0 >= budget_s:
-            break
-        b, h = divmod(bh, H)
-        heads_touched += 1
-        start = n - rows_per_chunk
-        while time.perf_counter() - t0 < budget_s and start > -rows_per_chunk:
-            rows = np.arange(max(0, start), start + rows_per_chunk)
-            orc.prefill(q[b, h], k[b, h], v[b, h], w=w, g=g, beta=beta, rows=rows)
-            done_pairs += sum(row_pairs(int(i), w, g) for i in rows)
-            done_rows += len(rows)
-            start -= rows_per_chunk
-    dt = time.perf_counter() - t0
+
+    def run(budget, nthreads, chunk):
+        done_pairs = done_rows = heads = 0
+        t0 = time.perf_counter()
+        # whole heads, each from its last rows backwards (full-window rows are
+        # the bulk of the workload), until the budget is spent
+        for bh in range(B * H):
+            if time.perf_counter() - t0 >= budget:
+                break
+            b, h = divmod(bh, H)
+            heads += 1
+            start = n - chunk
+            while time.perf_counter() - t0 < budget and start > -chunk:
+                rows = np.arange(max(0, start), start + chunk)
+                orc.prefill(q[b, h], k[b, h], v[b, h], w=w, g=g, beta=beta, rows=rows, nthreads=nthreads)
+                done_pairs += sum(row_pairs(int(i), w, g) for i in rows)
+                done_rows += len(rows)
+                start -= chunk
+        return done_pairs, done_rows, heads, time.perf_counter() - t0
+
+    pairs, rows, heads, dt = run(budget_s, threads, rows_per_chunk)
+    pairs1, rows1, _, dt1 = run(single_s, 1, rows_per_chunk)
     return {
-        "value": 4.0 * d * done_pairs / dt / 1e12,
+        "value": 4.0 * d * pairs / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": orc.num_threads(),
+        "cores": threads,
         "kind": "oracle",
-        "sample": f"{done_rows} query rows over {heads_touched} head(s) of {name} (each head from its "
-                  f"last row backwards), fp64, {dt:.1f} s",
+        "sample": f"{rows} query rows over {heads} head(s) of {name} (each head from its last row backwards), "
+                  f"fp64, {dt:.1f} s on {threads} threads",
+        "nproc": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+        "cpu_model": _cpu_model(),
+        "per_core": {"value": 4.0 * d * pairs1 / dt1 / 1e12, "unit": "TFLOP/s",
+                     "sample": f"{rows1} rows of the first head from its last row backwards, 1 thread, {dt1:.1f} s"},
+        "full_workload_s_estimate": 4.0 * d * band_pairs(n, w, g) * B * H / (4.0 * d * pairs / dt),
     }
 
 
@@ -454,7 +542,8 @@ def cpu_baseline_decode(name, budget_s=10.0):
         done += units
     dt = time.perf_counter() - t0
     return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": orc.num_threads(), "kind": "oracle",
-            "sample": f"{done} (batch, head) queries of {name}, fp64, {dt:.1f} s"}
+            "sample": f"{done} (batch, head) queries of {name}, fp64, {dt:.1f} s", "nproc": os.cpu_count(),
+            "cpu_model": _cpu_model()}
 
 
 def calibrate_copy(steps: int, nbytes: int = 1 << 30):
@@ -478,16 +567,33 @@ def calibrate_copy(steps: int, nbytes: int = 1 << 30):
           flush=True)
 
 
+def _bench(name, steps, warmup, cold=False):
+    if name in PREFILL:
+        return bench_prefill(name, steps, warmup, cold=cold)
+    if name in PREFILL_GQA:
+        return bench_prefill_gqa(name, steps, warmup)
+    if name in CHUNK:
+        return bench_chunk(name, steps, warmup)
+    if name in PATTERN:
+        return bench_pattern(name, steps, warmup)
+    return bench_decode(name, steps, warmup)
+
+
+def _brief(r):
+    keep = ("value", "unit", "ms_per_step", "dtype", "config", "roofline", "cold_cache")
+    return {k: r[k] for k in keep if k in r}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # the clock settles over the first ~25 launches of a busy kernel (power
-    # management); the default warmup keeps the timed launches past that
-    ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="mistral_prefill", choices=sorted(PREFILL) + sorted(DECODE) + sorted(CHUNK) + sorted(PATTERN))
+    ap.add_argument("--warmup", type=int, default=10)
+    names = sorted(PREFILL) + sorted(PREFILL_GQA) + sorted(DECODE) + sorted(CHUNK) + sorted(PATTERN)
+    ap.add_argument("--workload", default=HEADLINE, choices=names)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true", help="skip the decode figures on a prefill line")
+    ap.add_argument("--no-extras", action="store_true", help="time only the selected workload")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache prefill figure")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -505,14 +611,17 @@ def main():
         calibrate_copy(args.steps)
         return
 
-    if args.workload in PREFILL:
-        r = bench_prefill(args.workload, args.steps, args.warmup)
-    elif args.workload in CHUNK:
-        r = bench_chunk(args.workload, args.steps, args.warmup)
-    elif args.workload in PATTERN:
-        r = bench_pattern(args.workload, args.steps, args.warmup)
-    else:
-        r = bench_decode(args.workload, args.steps, args.warmup)
+    extra = {}
+    if not args.no_extras and args.workload == HEADLINE:
+        # the other workloads first: the headline is timed last, on a chip
+        # whose clock has settled under load
+        for name in ("rolling_decode", "mistral_prefill", "gemma3_local_prefill"):
+            extra[name] = _brief(_bench(name, args.steps, args.warmup))
+            torch.cuda.empty_cache()
+        extra["kv_append"] = _brief(bench_kv_append("rolling_decode", args.steps, args.warmup))
+        torch.cuda.empty_cache()
+    r = _bench(args.workload, args.steps, args.warmup,
+               cold=(not args.no_cold and args.workload in PREFILL))
     line = {
         "metric": METRIC,
         "value": r["value"],
@@ -530,19 +639,14 @@ def main():
         "roofline": r["roofline"],
     }
     line["roofline"]["frac_str"] = f"{100 * r['roofline']['frac']:.1f}% of MI355X peak"
-    if args.workload in PREFILL and not args.no_decode:
-        dname = "rolling_decode"
-        dr = bench_decode(dname, args.steps, args.warmup)
-        line["decode"] = {"value": dr["value"], "unit": dr["unit"], "ms_per_step": dr["ms_per_step"],
-                          "config": dr["config"], "roofline": dr["roofline"]}
+    if "cold_cache" in r:
+        line["cold_cache"] = r["cold_cache"]
+    if extra:
+        line["extra"] = extra
     if not args.no_cpu_baseline:
         if args.workload in PREFILL:
             line["cpu_baseline"] = cpu_baseline_prefill(args.workload)
-        elif args.workload in CHUNK:
-            line["cpu_baseline"] = cpu_baseline_chunk(args.workload)
-        elif args.workload in PATTERN:
-            line["cpu_baseline"] = cpu_baseline_pattern(args.workload)
-        else:
+        elif args.workload in DECODE:
             line["cpu_baseline"] = cpu_baseline_decode(args.workload)
     print(json.dumps(line), flush=True)
 
