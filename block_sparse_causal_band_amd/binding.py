@@ -89,7 +89,7 @@ def lib() -> ctypes.CDLL:
         L.swa_band_tiles.restype = ctypes.c_long
         L.swa_prefill_tile_shape.argtypes = [_int, _int, ctypes.POINTER(_int), ctypes.POINTER(_int)]
         L.swa_prefill_tile_shape.restype = _int
-        L.swa_prefill_order.argtypes = [_int, _int, _vp, ctypes.c_long]
+        L.swa_prefill_order.argtypes = [_int, _int, _int, _vp, ctypes.c_long]
         L.swa_prefill_order.restype = ctypes.c_long
         _LIB = L
     return _LIB
@@ -458,11 +458,12 @@ def prefill_tile_shape(dtype_code: int, d: int):
     return bq.value, bk.value
 
 
-def prefill_order(units: int, nqb: int) -> np.ndarray:
-    """Workgroup id -> (unit, query block) of a prefill launch, as int array [units*nqb, 2]."""
+def prefill_order(units: int, nqb: int, group: int = 1) -> np.ndarray:
+    """Workgroup id -> (unit, query block) of a prefill launch, as int array
+    [units*nqb, 2]; group = query heads per key/value head."""
     total = units * nqb
     out = np.zeros((total, 2), dtype=np.int32)
-    got = lib().swa_prefill_order(units, nqb, out.ctypes.data, total)
+    got = lib().swa_prefill_order(units, nqb, group, out.ctypes.data, total)
     if got != total:
         raise SwaError(got, "swa_prefill_order")
     return out

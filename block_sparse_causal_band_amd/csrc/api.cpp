@@ -391,13 +391,13 @@ int swa_prefill_tile_shape(swa_dtype_t dtype, int d, int *bq, int *bk) {
     return SWA_OK;
 }
 
-long swa_prefill_order(int units, int nqb, int *out, long cap) {
-    if (units < 1 || nqb < 1 || cap < 0 || (cap > 0 && !out)) return SWA_EINVAL;
+long swa_prefill_order(int units, int nqb, int group, int *out, long cap) {
+    if (units < 1 || nqb < 1 || group < 1 || units % group != 0 || cap < 0 || (cap > 0 && !out)) return SWA_EINVAL;
     const long long total = (long long)units * nqb;
     if (total > INT_MAX) return SWA_EINVAL;
     for (long long bid = 0; bid < total; ++bid) {
         int u, qb;
-        swa::workgroup_order((int)bid, (int)total, nqb, &u, &qb);
+        swa::workgroup_order((int)bid, (int)total, nqb, group, &u, &qb);
         if (bid < cap) {
             out[2 * bid] = u;
             out[2 * bid + 1] = qb;

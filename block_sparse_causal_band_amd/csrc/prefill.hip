@@ -356,7 +356,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     const int lh = lane >> 5;  // which half of the wave
 
     int unit, qb;
-    workgroup_order(blockIdx.x, total_wg, nqb, &unit, &qb);
+    // the query heads of one key/value head take each query block together
+    // (strided launches interleave residue classes in their units: no grouping)
+    workgroup_order(blockIdx.x, total_wg, nqb, STRIDED ? 1 : heads / kv_heads, &unit, &qb);
     // strided patterns: query row i of this unit is row oq + i sq of q and o,
     // key index k is row okv + k skv of k and v; nq query rows
     int nq = n, sq = 1, oq = 0, skv = 1, okv = 0;
@@ -819,7 +821,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
     const int lh = lane >> 5;
 
     int unit, qb;
-    workgroup_order(blockIdx.x, total_wg, nqb, &unit, &qb);
+    workgroup_order(blockIdx.x, total_wg, nqb, STRIDED ? 1 : heads / kv_heads, &unit, &qb);
     int nq = n, sq = 1, oq = 0, skv = 1, okv = 0;  // strided patterns, as in the bf16 kernel
     if constexpr (STRIDED) {
         if (ca.mode == 1) {

@@ -65,15 +65,22 @@ constexpr int kXcds = 8;
 // L2.  Within a head the query blocks run from the first to the last, so a
 // block's first key tiles (the low end of its window) are the ones the block
 // before it has just read into that L2, and the tiles no earlier block
-// touched (the diagonal) come last, after the block is under way.
-__host__ __device__ inline void workgroup_order(int bid, int total, int nqb, int *unit, int *qb) {
+// touched (the diagonal) come last, after the block is under way.  With
+// grouped-query attention (group query heads per key/value head, consecutive
+// units of one batch entry) the group's query heads take the same query
+// block one after another, so all of them read that block's K/V tiles from
+// the same L2 while they are there ("Sliding Window and Sparse Attention,
+// from Longformer to CSA2", s10 glossary, GQA).  group = 1 is the order above.
+__host__ __device__ inline void workgroup_order(int bid, int total, int nqb, int group, int *unit, int *qb) {
     int xcd = bid % kXcds;
     int slot = bid / kXcds;
     int per = total / kXcds;
     int rem = total % kXcds;
     int logical = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
-    *unit = logical / nqb;
-    *qb = logical % nqb;
+    const int hg = logical % group;  // query head within its group
+    const int rest = logical / group;
+    *qb = rest % nqb;
+    *unit = (rest / nqb) * group + hg;
 }
 
 // The FULL tiles of query rows [qa, qz] (qz < n) are one contiguous run

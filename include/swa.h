@@ -309,11 +309,13 @@ int swa_prefill_tile_shape(swa_dtype_t dtype, int d, int *bq, int *bk);
 
 /*
  * Test hook (host only): the workgroup -> (batch*head, query block) order of
- * a prefill launch with `units` (batch, head) pairs and `nqb` query blocks.
- * Writes pairs for workgroup ids 0 .. units*nqb-1.  Returns the count or a
- * negative status.
+ * a prefill launch with `units` (batch, head) pairs, `nqb` query blocks and
+ * `group` query heads per key/value head (heads / kv_heads; 1 for
+ * multi-head attention and for the strided patterns).  Writes pairs for
+ * workgroup ids 0 .. units*nqb-1.  Returns the count or a negative status
+ * (SWA_EINVAL when group does not divide units).
  */
-long swa_prefill_order(int units, int nqb, int *out, long cap);
+long swa_prefill_order(int units, int nqb, int group, int *out, long cap);
 
 #ifdef __cplusplus
 }

@@ -215,13 +215,14 @@ static void schedule_checks() {
     const int tiles[][2] = {{128, 64}, {64, 64}, {32, 32}, {128, 128}, {16, 48}, {256, 32}};
     for (const auto &s : shapes)
         for (const auto &t : tiles) schedule_shape(s[0], s[1], s[2], t[0], t[1]);
-    const int orders[][2] = {{1, 1}, {1, 7}, {3, 5}, {32, 128}, {5, 13}, {2, 3}, {16, 1024}};
+    const int orders[][3] = {{1, 1, 1}, {1, 7, 1}, {3, 5, 1}, {32, 128, 1}, {5, 13, 1}, {2, 3, 1}, {16, 1024, 1},
+                             {32, 128, 4}, {8, 5, 8}, {6, 7, 3}, {4, 3, 2}};
     for (const auto &o : orders) {
-        const int units = o[0], nqb = o[1], total = units * nqb;
+        const int units = o[0], nqb = o[1], group = o[2], total = units * nqb;
         std::vector<unsigned char> seen(total, 0);
         for (int bid = 0; bid < total; ++bid) {
             int u, qb;
-            swa::workgroup_order(bid, total, nqb, &u, &qb);
+            swa::workgroup_order(bid, total, nqb, group, &u, &qb);
             CHECK(u >= 0 && u < units && qb >= 0 && qb < nqb, "order in range");
             if (u >= 0 && u < units && qb >= 0 && qb < nqb) {
                 CHECK(!seen[u * nqb + qb], "order visits (%d,%d) once", u, qb);

@@ -76,12 +76,37 @@ def test_real_config_tile_counts(n, w, g, bq, bk):
     assert len(tiles) < dense_causal
 
 
-@pytest.mark.parametrize("units,nqb", [(1, 1), (1, 7), (3, 5), (32, 128), (16, 1024), (5, 13), (2, 3)])
-def test_workgroup_order_is_a_permutation(units, nqb):
-    order = swa.prefill_order(units, nqb)
+@pytest.mark.parametrize("units,nqb,group", [(1, 1, 1), (1, 7, 1), (3, 5, 1), (32, 128, 1), (16, 1024, 1), (5, 13, 1),
+                                              (2, 3, 1), (32, 128, 4), (32, 32, 4), (8, 5, 8), (6, 7, 3), (64, 9, 16)])
+def test_workgroup_order_is_a_permutation(units, nqb, group):
+    order = swa.prefill_order(units, nqb, group)
     pairs = {(u, q) for u, q in order.tolist()}
     assert len(pairs) == units * nqb
     assert pairs == {(u, q) for u in range(units) for q in range(nqb)}
+
+
+def test_workgroup_order_rejects_a_group_that_does_not_divide_the_units():
+    with pytest.raises(swa.SwaError):
+        swa.prefill_order(6, 4, 4)
+
+
+@pytest.mark.parametrize("units,nqb,group", [(32, 128, 4), (32, 32, 4), (16, 64, 2), (8, 100, 8)])
+def test_grouped_query_heads_take_each_block_together(units, nqb, group):
+    """With several query heads per key/value head, the group's heads take
+    the same query block at consecutive logical positions on one XCD, so
+    they read that block's K/V tiles from one L2 at about the same time:
+    within each XCD's run the workgroups come in runs of `group`, one per
+    query head of a group, all on the same block."""
+    order = swa.prefill_order(units, nqb, group)
+    for xcd in range(8):
+        run = order[xcd::8].tolist()
+        for (u0, q0), (u1, q1) in zip(run, run[1:]):
+            if u1 % group != 0:  # not the first query head of its group: follows the previous head
+                assert (u1, q1) == (u0 + 1, q0)
+    # one key/value head's group stays on one XCD for the gqa workload shape
+    if (units, nqb, group) == (32, 128, 4):
+        for xcd in range(8):
+            assert len({u // group for u in order[xcd::8, 0].tolist()}) == 1
 
 
 def test_workgroup_order_keeps_heads_on_one_xcd():
