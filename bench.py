@@ -92,9 +92,16 @@ PATTERN = {
 # the source has changed since, the figure no longer describes the kernel and
 # `traffic` is reported as null.
 MEASURED_TRAFFIC = {
-    "rolling_decode": {"bytes": 4300265431, "source_digest": "1197048432c9c06b"},
-    "gqa_decode": {"bytes": 1076057369, "source_digest": "1197048432c9c06b"},
-    "fp8_decode": {"bytes": 2151013950, "source_digest": "1197048432c9c06b"},
+    "sink_prefill": {"bytes": 1074245697, "source_digest": "79a1d31e79b97b17"},
+    "mistral_prefill": {"bytes": 537759176, "source_digest": "79a1d31e79b97b17"},
+    "gemma3_local_prefill": {"bytes": 2213233591, "source_digest": "79a1d31e79b97b17"},
+    "gqa_prefill": {"bytes": 336036239, "source_digest": "79a1d31e79b97b17"},
+    "chunk_prefill": {"bytes": 117720138, "source_digest": "79a1d31e79b97b17"},
+    "dilated_prefill": {"bytes": 541697007, "source_digest": "79a1d31e79b97b17"},
+    "landmark_prefill": {"bytes": 948370776, "source_digest": "79a1d31e79b97b17"},
+    "rolling_decode": {"bytes": 4300158521, "source_digest": "be64c163c11ea9c2"},
+    "gqa_decode": {"bytes": 1076026282, "source_digest": "be64c163c11ea9c2"},
+    "fp8_decode": {"bytes": 2150936125, "source_digest": "be64c163c11ea9c2"},
 }
 # Matrix-core figures of the prefill kernels from rocprofv3 counter runs
 # (SQ_INSTS_MFMA, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, SQ_BUSY_CYCLES per
@@ -103,7 +110,18 @@ MEASURED_TRAFFIC = {
 #   issued_per_band: MFMA FLOP issued (SQ_INSTS_MFMA x 32768) / band FLOP;
 #   mfma_busy_per_simd: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs);
 #   clock_ghz: GRBM_GUI_ACTIVE / 8 XCDs / kernel duration.
-MEASURED_COUNTERS: dict = {}
+MEASURED_COUNTERS = {
+    "sink_prefill": {"issued_per_band": 1.0448, "mfma_busy_per_simd": 0.5903, "clock_ghz": 1.823,
+                     "valu_per_mfma": 4.78, "source_digest": "79a1d31e79b97b17"},
+    "mistral_prefill": {"issued_per_band": 1.0312, "mfma_busy_per_simd": 0.5611, "clock_ghz": 1.867,
+                        "valu_per_mfma": 4.72, "source_digest": "79a1d31e79b97b17"},
+    "gemma3_local_prefill": {"issued_per_band": 1.125, "mfma_busy_per_simd": 0.4904, "clock_ghz": 1.91,
+                             "valu_per_mfma": 5.97, "source_digest": "79a1d31e79b97b17"},
+    "gqa_prefill": {"issued_per_band": 1.0312, "mfma_busy_per_simd": 0.5728, "clock_ghz": 1.852,
+                    "valu_per_mfma": 4.72, "source_digest": "79a1d31e79b97b17"},
+    "chunk_prefill": {"issued_per_band": 1.0537, "mfma_busy_per_simd": 0.5568, "clock_ghz": 1.846,
+                      "valu_per_mfma": 4.9, "source_digest": "79a1d31e79b97b17"},
+}
 CSRC = os.path.join(ROOT, "block_sparse_causal_band_amd", "csrc")
 
 
