@@ -392,7 +392,7 @@ def bench_pattern(name, steps, warmup):
                    "r": r, "sink_bias": beta, "band_flops_per_step": flops},
         "roofline": _roofline("mfma", flops, per, PEAK_BF16_TFLOPS, "TFLOP/s", None,
                               ("prefill_bf16_kernel<128,strided> (dilated classes)" if kind == "dilated" else
-                               "window prefill + landmark part merged in its epilogue (one call, two launches)")),
+                               "prefill_bf16_kernel<128,landmark> (landmark tiles, then window and sink tiles, one launch)")),
     }
 
 

@@ -29,8 +29,10 @@ hipError_t launch_dilated_prefill(const void *q, const void *k, const void *v, v
                                   hipStream_t stream);
 hipError_t launch_landmark_part(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
                                 int heads, int kv_heads, int n, int d, int w, int g, int r, float scale, bool bf16,
-                                hipStream_t stream, void *merge_o = nullptr, const float *merge_lse = nullptr,
-                                float *merged_lse = nullptr);
+                                hipStream_t stream);
+hipError_t launch_landmark_prefill(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
+                                   int heads, int kv_heads, int n, int d, int w, int g, int r, float scale,
+                                   float sink_bias, hipStream_t stream);
 hipError_t launch_kv_append_fp8(void *kc, void *vc, const void *kn, const void *vn, const int64_t *pos,
                                 const float *ksc, const float *vsc, int batch, int heads, int tn, int d, int w,
                                 int g, bool bf16, hipStream_t stream);
@@ -159,9 +161,9 @@ int swa_dilated_prefill_fwd(const void *q, const void *k, const void *v, void *o
 size_t swa_landmark_workspace_bytes(int batch, int heads, int n, int d, swa_dtype_t dtype) {
     if (batch < 1 || heads < 1 || n < 1 || (d != 64 && d != 128) || (dtype != SWA_F32 && dtype != SWA_BF16))
         return 0;
+    if (dtype == SWA_BF16) return 0;  // one launch over landmark, window and sink tiles
     const size_t rows = (size_t)batch * heads * n;
     const size_t lb = (rows * 4 + 255) / 256 * 256;
-    if (dtype == SWA_BF16) return lb;  // the window part's LSE (the landmark part merges in its epilogue)
     const size_t ob = (rows * d * 4 + 255) / 256 * 256;
     return ob + 2 * lb;  // fp32: the landmark part's o and both LSEs, merged by a third launch
 }
@@ -174,22 +176,16 @@ int swa_landmark_prefill_fwd(const void *q, const void *k, const void *v, void *
     int st = check_prefill(q, k, v, o, lse, batch, heads, kv_heads, n, d, w, g, scale, sink_bias, dtype, 1);
     if (st != SWA_OK) return st;
     const size_t need = swa_landmark_workspace_bytes(batch, heads, n, d, dtype);
-    if (!workspace || workspace_bytes < need) return SWA_EWORKSPACE;
-    if (!aligned16(workspace)) return SWA_EALIGN;
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return SWA_EWORKSPACE;
+        if (!aligned16(workspace)) return SWA_EALIGN;
+    }
     const bool bf16 = dtype == SWA_BF16;
+    if (bf16)
+        return status_of(swa::launch_landmark_prefill(q, k, v, o, lse, batch, heads, kv_heads, n, d, w, g, r, scale,
+                                                      sink_bias, stream));
     const size_t rows = (size_t)batch * heads * n;
     uint8_t *ws = static_cast<uint8_t *>(workspace);
-    if (bf16) {
-        // window and sinks into o (its LSE into the workspace), then the
-        // landmark part, merged into o by LSE in its own epilogue
-        float *lse_a = reinterpret_cast<float *>(ws);
-        hipError_t e = swa::launch_prefill(q, k, v, o, lse_a, batch, heads, kv_heads, n, d, w, g, scale, sink_bias,
-                                           true, stream);
-        if (e == hipSuccess)
-            e = swa::launch_landmark_part(q, k, v, o, nullptr, batch, heads, kv_heads, n, d, w, g, r, scale, true,
-                                          stream, o, lse_a, lse);
-        return status_of(e);
-    }
     void *o_b = ws;
     float *lse_a = reinterpret_cast<float *>(ws + (rows * d * (bf16 ? 2 : 4) + 255) / 256 * 256);
     float *lse_b = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(lse_a) + (rows * 4 + 255) / 256 * 256);

@@ -101,21 +101,20 @@ __device__ __forceinline__ size_t kv_offset(int unit, int heads, int kv_heads, i
 //  * landmark part (mode 2): query i reads the landmarks j = k r that lie
 //    below its window and are not sinks (g <= j <= i-w); over the K/V rows
 //    strided by r that is the compact index range ceil(g/r) <= k <=
-//    floor((i-w)/r).  The window-and-sinks part is an ordinary launch; the
-//    two parts merge by LSE.
-enum { kPlain = 0, kChunk = 1, kStrided = 2 };
+//    floor((i-w)/r).  The fp32 path runs it as a launch of its own and merges
+//    it with the window-and-sinks launch by LSE.
+//  * landmarks in one pass (kLandmark, bf16): each query block first streams
+//    the tiles of that compact landmark range (K/V rows strided by r) and then
+//    its window-and-sink tiles, all through one online softmax, so the union
+//    of the three key sets is attended in a single launch.
+enum { kPlain = 0, kChunk = 1, kStrided = 2, kLandmark = 3 };
 struct PathArgs {
     const void *kc;        // chunk: K cache [batch][kv_heads][g + w][d]
     const void *vc;        // chunk: V cache, same layout
     const int64_t *pos;    // chunk: p0 of each batch entry
     int part;              // chunk: which keys
-    int r;                 // strided: the stride
+    int r;                 // strided, landmarks: the stride
     int mode;              // strided: 1 dilated, 2 landmark part
-    // landmark part (bf16) merged into the window part's result: o of the
-    // window part, merged in place; its LSE; where the merged LSE goes (or null)
-    uint16_t *mo;
-    const float *mla;
-    float *mlo;
 };
 constexpr int kNoWindow = 1 << 30;  // a window wider than any sequence
 
@@ -163,6 +162,20 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int qi, int k0, int lh
             const int j = k0 + 32 * sb + 8 * (r >> 2) + 4 * lh + (r & 3);
             const float x = s[sb][r] + (j < g ? bias_raw : 0.f);
             s[sb][r] = (pair_attended(qi, j, n, w, g) && (!KLO || j >= klo)) ? x : kNegInf;
+        }
+}
+
+// Landmark tile of the single-pass landmark kernel: compact landmark index j
+// (key row j r) is read by a row iff lk_lo <= j <= lq, lq being the row's last
+// landmark below its window (-1 when it has none); landmarks are >= g, so no
+// sink bias.
+__device__ __forceinline__ void mask_landmark_tile(f32x16 (&s)[2], int lq, int k0, int lh, int lk_lo) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int j = k0 + 32 * sb + 8 * (r >> 2) + 4 * lh + (r & 3);
+            s[sb][r] = (j >= lk_lo && j <= lq) ? s[sb][r] : kNegInf;
         }
 }
 
@@ -252,64 +265,6 @@ __device__ __forceinline__ void store_rows_lds(const f32x16 (&oacc)[D / 32], flo
     if (lse != nullptr && lh == 0 && qi < nq) lse[(size_t)qi * rs] = m_run * scale + logf(l_tot);
 }
 
-// The landmark part of a landmark launch, merged in its epilogue into the
-// window part's result by LSE, with the arithmetic of lse_merge_kernel: the
-// rows of this part are staged in LDS as bf16 exactly as store_rows_lds
-// writes them, with their LSE m * scale + ln l (-inf where the row has no
-// landmark); each lane then merges 8 values of a row with the window part's
-// o and LSE and writes o (in place) and the merged LSE.
-template <int D>
-__device__ __forceinline__ void merge_rows_lds(const f32x16 (&oacc)[D / 32], float m_run, float l_run, int qw0,
-                                               int nq, int lr, int lh, int lane, uint16_t *O, const float *la,
-                                               float *lo, float scale, uint8_t *region, float *lreg) {
-    constexpr int RB = 2 * D;
-    constexpr int CPR = RB / 16;
-    const float l_tot = half_swap_sum(l_run);
-    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-#pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-            const int ch = 4 * cb + gq;
-            const float x0 = oacc[cb][4 * gq + 0] * inv, x1 = oacc[cb][4 * gq + 1] * inv;
-            const float x2 = oacc[cb][4 * gq + 2] * inv, x3 = oacc[cb][4 * gq + 3] * inv;
-            *reinterpret_cast<uint2 *>(region + lr * RB + ((ch ^ (lr % CPR)) * 16) + 8 * lh) =
-                make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
-        }
-    if (lh == 0) lreg[lr] = m_run * scale + logf(l_tot);
-#pragma unroll
-    for (int j = 0; j < 32 * CPR / 64; ++j) {
-        const int idx = 64 * j + lane;
-        const int r = idx / CPR, ch = idx % CPR;
-        const int row = qw0 + r;
-        if (row >= nq) continue;
-        const uint4 vb = *reinterpret_cast<const uint4 *>(region + r * RB + ((ch ^ (r % CPR)) * 16));
-        const float a = la[row], b = lreg[r];
-        const float M = fmaxf(a, b);
-        float wa = 0.f, wb = 0.f;
-        if (M != kNegInf) {
-            wa = fast_exp2((a - M) * (float)kLog2e);
-            wb = fast_exp2((b - M) * (float)kLog2e);
-        }
-        const float sum = wa + wb;
-        const float sinv = (sum > 0.f) ? 1.f / sum : 0.f;
-        wa *= sinv;
-        wb *= sinv;
-        uint16_t *orow = O + (size_t)row * D + 8 * ch;
-        const uint4 va = *reinterpret_cast<const uint4 *>(orow);
-        const uint32_t ua[4] = {va.x, va.y, va.z, va.w}, ub[4] = {vb.x, vb.y, vb.z, vb.w};
-        uint32_t res[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float r0 = (wa > 0.f ? wa * bf16lo(ua[e]) : 0.f) + (wb > 0.f ? wb * bf16lo(ub[e]) : 0.f);
-            const float r1 = (wa > 0.f ? wa * bf16hi(ua[e]) : 0.f) + (wb > 0.f ? wb * bf16hi(ub[e]) : 0.f);
-            res[e] = pack_bf16x2(r0, r1);
-        }
-        *reinterpret_cast<uint4 *>(orow) = make_uint4(res[0], res[1], res[2], res[3]);
-        if (lo != nullptr && ch == 0) lo[row] = (sum > 0.f) ? M + logf(sum) : kNegInf;
-    }
-}
-
 // ---------------------------------------------------------------------------
 // bf16 path.
 template <int D, int WAVES>
@@ -332,13 +287,14 @@ struct Bf16Tile {
 
 // KIND kChunk: the queries are a chunk of n positions starting at p0 =
 // pos[b] and the keys come from the chunk and the cache; kStrided: a strided
-// pattern (PathArgs); kPlain: q, k, v are whole sequences of n positions.
+// pattern (PathArgs); kLandmark: window, sinks and landmarks every ca.r in one
+// pass; kPlain: q, k, v are whole sequences of n positions.
 template <int D, int WAVES, int KIND>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp, const uint16_t *__restrict__ vp,
     uint16_t *__restrict__ op, float *__restrict__ lsep, int n, int nqb, int w, int g, float c2, float scale,
     float bias_raw, int total_wg, int heads, int kv_heads, PathArgs ca) {
-    constexpr bool CHUNK = (KIND == kChunk), STRIDED = (KIND == kStrided);
+    constexpr bool CHUNK = (KIND == kChunk), STRIDED = (KIND == kStrided), LAND = (KIND == kLandmark);
     using L = Bf16Tile<D, WAVES>;
     constexpr int BQ = 32 * WAVES;
     // two K and two V tile buffers, as four arrays: the compiler can then see
@@ -424,7 +380,19 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     };
     const int qa = qpos(qi);  // position of this lane's query row
     const BandRange band = band_range(qpos(q0), qpos(q1), wq, g, kBK);
-    const int ntiles = band.count();
+    // kLandmark: tiles 0 .. nl-1 hold compact landmark indices (lb0 + t) * kBK
+    // .. +kBK-1 (K/V rows k * ca.r), covering lk_lo .. the block's last row's
+    // last landmark; the window-and-sink tiles follow as tiles nl ..
+    int nl = 0, lb0 = 0, lk_lo = 0;
+    if constexpr (LAND) {
+        lk_lo = (g + ca.r - 1) / ca.r;  // landmarks below g are sinks
+        const int lq1 = (q1 >= w) ? (q1 - w) / ca.r : -1;
+        if (lq1 >= lk_lo) {
+            lb0 = lk_lo / kBK;
+            nl = lq1 / kBK - lb0 + 1;
+        }
+    }
+    const int ntiles = nl + band.count();
     const float tau = 8.f / c2;
 
     // ---- Q of this wave's 32 rows as the B operand (kept in VGPRs) ----
@@ -465,6 +433,21 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < L::kDmaPerWave; ++i) dma16(r, dst + (wave * L::kDmaPerWave + i) * 1024, offs[i]);
     };
+    // landmark tile: compact indices k0 .. k0+63, rows k * ca.r (the offsets
+    // above are key * row bytes + chunk; the row is re-formed in 64 bits and
+    // clamped as for a strided launch)
+    auto dma_land = [&](bool is_k, int k0, uint8_t *dst) {
+        const uint16_t *src = is_k ? K : V;
+        const uint32_t *offs = is_k ? dma_k : dma_v;
+        const int r0 = k0 * ca.r;  // < n: tile nl-1 holds a landmark below n
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)r0 * D, (uint32_t)(n - r0) * L::kRowBytes);
+#pragma unroll
+        for (int i = 0; i < L::kDmaPerWave; ++i) {
+            const uint32_t key = offs[i] / L::kRowBytes;
+            const uint32_t part = offs[i] - key * L::kRowBytes;
+            dma16(r, dst + (wave * L::kDmaPerWave + i) * 1024, row_off((uint64_t)key * ca.r, n, L::kRowBytes) + part);
+        }
+    };
     // tile of key positions k0 .. k0+63 of K (or V) into LDS at dst
     auto dma = [&](bool is_k, int k0, uint8_t *dst) {
         const uint16_t *src = is_k ? K : V;
@@ -494,6 +477,27 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
                 }
             }
         }
+    };
+
+    // tile t of the block's sequence: landmark tiles first (kLandmark), then
+    // the window-and-sink tiles.  MAYBE_LAND false: t is known to be past the
+    // landmark tiles.
+    auto key_block = [&](int t) -> int {
+        if constexpr (LAND) {
+            if (t < nl) return lb0 + t;
+            return band.block(t - nl);
+        }
+        return band.block(t);
+    };
+    auto dma_t = [&](bool is_k, int t, uint8_t *dst, auto maybe_land_tag) __attribute__((always_inline)) {
+        if constexpr (LAND && decltype(maybe_land_tag)::value) {
+            if (t < nl) {
+                dma_land(is_k, (lb0 + t) * kBK, dst);
+                return;
+            }
+        }
+        if constexpr (LAND) t -= nl;
+        dma(is_k, band.block(t) * kBK, dst);
     };
 
     // Per-lane LDS read offsets within a buffer.
@@ -534,9 +538,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     // computes the scores of tile t+1.  During tile t the DMA fills K(t+2) into
     // the K buffer that K(t) left and V(t+1) into the V buffer that V(t-1)
     // left, so every DMA has a whole tile of time to land.
-    dma(true, band.block(0) * kBK, kbuf0);
-    dma(false, band.block(0) * kBK, vbuf0);
-    if (ntiles > 1) dma(true, band.block(1) * kBK, kbuf1);
+    dma_t(true, 0, kbuf0, std::true_type{});
+    dma_t(false, 0, vbuf0, std::true_type{});
+    if (ntiles > 1) dma_t(true, 1, kbuf1, std::true_type{});
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     f32x16 s_cur[2];
@@ -552,9 +556,11 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
         uint8_t *const knxt = par ? kbuf0 : kbuf1;
         uint8_t *const vcur = par ? vbuf1 : vbuf0;
         uint8_t *const vnxt = par ? vbuf0 : vbuf1;
-        const int k0 = band.block(t) * kBK;
-        if (t + 2 < ntiles) dma(true, band.block(t + 2) * kBK, kcur);
-        if (t + 1 < ntiles) dma(false, band.block(t + 1) * kBK, vnxt);
+        const int k0 = key_block(t) * kBK;
+        // only cut tiles can be landmark tiles or precede one
+        using ML = std::integral_constant<bool, MASKED>;
+        if (t + 2 < ntiles) dma_t(true, t + 2, kcur, ML{});
+        if (t + 1 < ntiles) dma_t(false, t + 1, vnxt, ML{});
 
         const uint8_t *kb = knxt;
         const uint8_t *vb = vcur + voff;
@@ -585,7 +591,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
         }
 
         if constexpr (MASKED) {
-            mask_tile<CHUNK || STRIDED>(s_cur, qa, k0, lh, khi, wq, g, bias_raw, klo);
+            if (LAND && t < nl)  // the row's last landmark below its window: (qi - w) / r
+                mask_landmark_tile(s_cur, (qa >= w) ? (qa - w) / ca.r : -1, k0, lh, lk_lo);
+            else
+                mask_tile<CHUNK || STRIDED>(s_cur, qa, k0, lh, khi, wq, g, bias_raw, klo);
             update_max(s_cur, m_run, negm, l_run, oacc, c2, tau);
         }
 
@@ -674,9 +683,13 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
 
     // FULL tiles for this wave's own 32 rows: the band edges of the
     // workgroup's block cut a single wave's rows in fewer tiles.
-    int t_lo = 0, t_hi = ntiles;  // a wave entirely past n keeps all tiles unmasked (nothing is stored)
+    // (a wave entirely past n keeps all window tiles unmasked: it stores
+    // nothing; landmark tiles always take the cut-tile body, whose DMA knows them)
+    int t_lo = 0, t_hi = band.count();
     const int qw0 = q0 + wave * 32;
     if (qw0 < nq) full_range(band, qpos(qw0), qpos(min(qw0 + 31, nq - 1)), khi, wq, g, kBK, &t_lo, &t_hi, klo);
+    t_lo += nl;
+    t_hi += nl;
     // The last tile runs on its own (no next tile to score) and with the
     // mask, which leaves a FULL tile's scores as they are.  (The chunk
     // kernel keeps the discarded score stream on its last tile: a separate
@@ -718,14 +731,6 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     // stages its rows in its own 32 * 2D bytes of the K buffers
     static_assert(2 * 32 * 2 * D <= L::kTileBytes, "two waves' rows per K buffer");
     uint8_t *const region = ((wave < 2) ? kbuf0 : kbuf1) + (wave & 1) * (32 * 2 * D);
-    if constexpr (STRIDED) {
-        if (ca.mode == 2 && ca.mo != nullptr) {
-            merge_rows_lds<D>(oacc, m_run, l_run, q0 + wave * 32, nq, lr, lh, lane, ca.mo + base,
-                              ca.mla + (size_t)unit * n, ca.mlo ? ca.mlo + (size_t)unit * n : nullptr, scale, region,
-                              reinterpret_cast<float *>(vbuf0) + 32 * wave);
-            return;
-        }
-    }
     store_rows_lds<D>(oacc, m_run, l_run, q0 + wave * 32, nq, lr, lh, lane, op + base + (size_t)oq * D,
                       lsep ? lsep + (size_t)unit * n + oq : nullptr, scale, sq, region);
 }
@@ -1003,6 +1008,8 @@ static hipError_t launch_prefill_t(const void *q, const void *k, const void *v, 
         else
             hipLaunchKernelGGL((prefill_bf16_kernel<64, kWaves16, KIND>), grid, block, 0, stream, qq, kk, vv, oo,
                                lse, n, nqb, w, g, c2, scale, bias_raw, total, heads, kv_heads, ca);
+    } else if constexpr (KIND == kLandmark) {
+        return hipErrorInvalidValue;  // bf16 only: fp32 runs the landmark part as a launch of its own
     } else {
         const int nqb = (nq_max + kBQ - 1) / kBQ;
         const int total = units * nqb;
@@ -1044,17 +1051,21 @@ hipError_t launch_dilated_prefill(const void *q, const void *k, const void *v, v
 }
 
 // Landmark part of window + sinks + landmarks every r: the landmarks below
-// the window and not below g (lse of rows without one: -inf, o = 0).  With
-// merge_o set (bf16 only) the part is not stored but merged by LSE into the
-// window part's result: merge_o (o, in place) and merge_lse, the merged LSE
-// going to merged_lse when that is not null (o and lse are then unused).
+// the window and not below g (lse of rows without one: -inf, o = 0).
 hipError_t launch_landmark_part(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
                                 int heads, int kv_heads, int n, int d, int w, int g, int r, float scale, bool bf16,
-                                hipStream_t stream, void *merge_o, const float *merge_lse, float *merged_lse) {
-    return launch_prefill_t<kStrided>(
-        q, k, v, o, lse, batch, heads, kv_heads, n, d, w, g, scale, 0.f, bf16,
-        PathArgs{nullptr, nullptr, nullptr, 0, r, 2, static_cast<uint16_t *>(merge_o), merge_lse, merged_lse}, 1, n,
-        stream);
+                                hipStream_t stream) {
+    return launch_prefill_t<kStrided>(q, k, v, o, lse, batch, heads, kv_heads, n, d, w, g, scale, 0.f, bf16,
+                                      PathArgs{nullptr, nullptr, nullptr, 0, r, 2}, 1, n, stream);
+}
+
+// Window + sinks + landmarks every r in one bf16 launch (landmark tiles, then
+// the window-and-sink tiles of each query block, one online softmax).
+hipError_t launch_landmark_prefill(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
+                                   int heads, int kv_heads, int n, int d, int w, int g, int r, float scale,
+                                   float sink_bias, hipStream_t stream) {
+    return launch_prefill_t<kLandmark>(q, k, v, o, lse, batch, heads, kv_heads, n, d, w, g, scale, sink_bias, true,
+                                       PathArgs{nullptr, nullptr, nullptr, 0, r, 0}, 1, n, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -271,13 +271,14 @@ int swa_decode_fwd_fp8(const void *q, const void *k_cache, const void *v_cache,
  *
  * swa_landmark_prefill_fwd: query i reads its window i-w+1 .. i, the sinks
  * 0 .. g-1 and the landmarks, every position j <= i with j mod r == 0, each
- * position once; sink_bias on positions < g.  Computed as the window-and-
- * sinks part into o, then the part over the landmarks below the window and
- * not below g, merged by LSE (the arithmetic of swa_lse_merge) into o: for
- * bf16 in the landmark launch's own epilogue (the workspace holds the first
- * part's LSE), for fp32 through the workspace and a merge launch.
+ * position once; sink_bias on positions < g.  bf16: one launch, in which
+ * each query block streams the tiles of its landmarks below the window (and
+ * not below g; K/V rows strided by r) and then its window-and-sink tiles
+ * through one online softmax; no workspace (0 bytes: workspace may be null).
+ * fp32: the window-and-sinks part into o, the landmark part into the
+ * workspace, merged into o by LSE (the arithmetic of swa_lse_merge).
  * workspace: at least swa_landmark_workspace_bytes(...) bytes, 16-byte
- * aligned (SWA_EWORKSPACE otherwise).
+ * aligned, when that size is not 0 (SWA_EWORKSPACE, SWA_EALIGN otherwise).
  */
 int swa_dilated_prefill_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                             int batch, int heads, int kv_heads, int n, int d, int w, int r,

@@ -292,16 +292,18 @@ def _landmark(**kw):
 
 @pytest.mark.parametrize("kw,want", [
     (dict(q=None), EINVAL), (dict(r=0), EINVAL), (dict(g=-1), EINVAL), (dict(bias=float("nan")), EINVAL),
-    (dict(d=48), EUNSUP), (dict(ws=None), EWS), (dict(wsb=100), EWS), (dict(ws=P + 8), EALIGN),
+    (dict(d=48), EUNSUP),
+    # fp32 merges through the workspace (bf16 needs none)
+    (dict(ws=None, dtype=0), EWS), (dict(wsb=100, dtype=0), EWS), (dict(ws=P + 8, dtype=0), EALIGN),
 ])
 def test_landmark_rejects(kw, want):
     assert _landmark(**kw) == want
 
 
 def test_landmark_workspace_size():
-    # bf16: the window part's fp32 lse rows, rounded up to 256 bytes (the landmark
-    # part merges in its epilogue); fp32: the landmark part's o plus two lse rows
-    assert swa.landmark_workspace_bytes(1, 2, 64, 128, 1) == 512
+    # bf16: none (one launch over landmark, window and sink tiles); fp32: the
+    # landmark part's o plus two lse rows, each rounded up to 256 bytes
+    assert swa.landmark_workspace_bytes(1, 2, 64, 128, 1) == 0
     assert swa.landmark_workspace_bytes(1, 2, 64, 128, 0) == 1 * 2 * 64 * 128 * 4 + 2 * 512
     assert swa.landmark_workspace_bytes(1, 2, 64, 96, 1) == 0
 

@@ -75,9 +75,41 @@ def test_landmark_vs_oracle(dtype, d, n, w, g, r, beta):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n,w,g,r,beta", [
+    (2000, 64, 10, 4, 1.0),   # 484 landmarks: eight landmark tiles per late block, sinks past one stride
+    (1000, 50, 0, 1, 0.0),    # every position a landmark: full causal attention
+    (777, 130, 5, 5, 1.5),    # sinks end on a landmark; ragged n
+    (1300, 200, 64, 3, -2.0), # 64 sinks: the landmark range starts inside the second tile
+    (4200, 4096, 4, 64, 4.0), # the window of the Mistral-shaped workload: one short landmark tile
+])
+def test_landmark_tiles_vs_oracle(d, n, w, g, r, beta):
+    """bf16 runs every landmark tile of a query block (K/V rows strided by r)
+    and then its window and sink tiles through one online softmax: many
+    landmark tiles, none, a range starting past tile 0, full causal."""
+    dev = _dev()
+    q, k, v = synth.qkv(1, 2, n, d, torch.bfloat16, seed=96, device=dev)
+    print(f"landmark bf16 d={d} n={n} w={w} g={g} r={r}", flush=True)
+    o, lse = swa.landmark_prefill(q, k, v, w=w, g=g, r=r, sink_bias=beta, return_lse=True)
+    torch.cuda.synchronize()
+    rows = None if n <= 1000 else sorted(set(range(0, n, 7)) | set(range(n - 130, n)))
+    _check(q, k, v, o, lse, "landmark", w, g, r, beta, rows=rows)
+
+
+def test_landmark_every_position_is_causal_attention():
+    """r = 1 makes every position below the window a landmark: the union is
+    plain causal attention (prefill with w >= n), up to rounding order."""
+    dev = _dev()
+    q, k, v = synth.qkv(1, 4, 700, 128, torch.bfloat16, seed=97, device=dev)
+    a, la = swa.landmark_prefill(q, k, v, w=40, g=0, r=1, return_lse=True)
+    b, lb = swa.prefill(q, k, v, w=700, g=0, return_lse=True)
+    torch.cuda.synchronize()
+    gate(a.float().cpu().numpy(), b.float().cpu().numpy(), torch.bfloat16, "landmark r=1 vs causal")
+    gate(la.cpu().numpy(), lb.cpu().numpy(), torch.bfloat16, "landmark r=1 vs causal lse")
+
+
+@pytest.mark.parametrize("d", [64, 128])
 def test_landmark_without_lse_output(d):
-    """Without an LSE output the window part's LSE goes to the workspace; o is
-    the same bit for bit."""
+    """o is the same bit for bit with and without an LSE output."""
     dev = _dev()
     q, k, v = synth.qkv(2, 2, 517, d, torch.bfloat16, seed=95, device=dev)
     a, _ = swa.landmark_prefill(q, k, v, w=64, g=4, r=32, sink_bias=2.0, return_lse=True)
