@@ -2,7 +2,7 @@
 """Throughput of exact causal sliding-window attention (+ sinks) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-extras] [--no-cold] [--no-cpu-baseline]
+                    [--no-extras] [--no-cold] [--no-cpu-baseline] [--no-peaks]
 
 Prints ONE JSON line.  The headline workload is the sink prefill: batch 1,
 32 heads, n=32768, d=128, w=4096, g=4 sink tokens with a +4 logit offset,
@@ -29,7 +29,10 @@ WRITE_SIZE (calibrated on a plain device copy), reported only while the
 kernel sources match the ones the counters were taken on; `roofline.counters`
 likewise carries the matrix-core figures of the same profiles.
 `cpu_baseline` is the fp64 oracle on a bounded sample of the headline
-workload, on all the host's cores and on one core.
+workload, on all the host's cores and on one core.  `measured_peak` holds
+what the measurement kernels of include/swa_probe.h reach on this chip (a
+dense bf16 MFMA stream, a streaming HBM read); each roofline states
+`frac_of_measured` beside `frac` (against the datasheet peak).
 """
 from __future__ import annotations
 
@@ -221,13 +224,66 @@ def _run(step, steps, warmup):
     return _events_time(step, steps, torch.cuda.current_stream())
 
 
+# rates the measurement kernels reach on this chip (filled by measured_peaks)
+MEASURED_PEAK = {}
+
+
 def _roofline(bound, work, per, peak, unit, traffic, kernel, counters=None):
     st = _stats(per)
     achieved = work / (st["mean"] * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
-    return {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
-            "traffic": traffic, "kernel": kernel, "launch_ms": st,
-            "frac_median": work / (st["median"] * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9) / peak,
-            "counters": counters}
+    r = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+         "traffic": traffic, "kernel": kernel, "launch_ms": st,
+         "frac_median": work / (st["median"] * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9) / peak,
+         "counters": counters}
+    if bound in MEASURED_PEAK and peak in (PEAK_BF16_TFLOPS, PEAK_HBM_GBS):
+        m = MEASURED_PEAK[bound]["value"]
+        r["measured_peak"] = m
+        r["frac_of_measured"] = achieved / m
+    return r
+
+
+def measured_peaks(reps: int = 10):
+    """The dense bf16 MFMA stream and the streaming HBM read of
+    include/swa_probe.h, each timed with HIP events over `reps` launches
+    after 3 warm-up launches; the read takes the best of a few launch shapes
+    over a 4 GiB buffer.  Fills MEASURED_PEAK and returns it."""
+    import torch
+
+    import block_sparse_causal_band_amd as swa
+
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+
+    wg, iters = 1024, 8000
+    out = torch.empty(wg * 256, dtype=torch.float32, device=dev)
+    flops = 0.0
+    for _ in range(3):
+        flops = swa.probe_mfma_bf16(out, wg, iters)
+    _, per = _events_time(lambda: swa.probe_mfma_bf16(out, wg, iters), reps, stream)
+    st = _stats(per)
+    MEASURED_PEAK["mfma"] = {"value": flops / (st["median"] * 1e-3) / 1e12, "unit": "TFLOP/s",
+                             "kernel": "probe_mfma_kernel (v_mfma_f32_32x32x16_bf16, register operands)",
+                             "workgroups": wg, "iters": iters, "launch_ms_median": st["median"]}
+    del out
+
+    nbytes = 1 << 32
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    best = None
+    for wg in (1024, 2048, 4096):
+        for streams in (1, 2):
+            sink = torch.zeros(wg, dtype=torch.int32, device=dev)
+            for _ in range(3):
+                swa.probe_hbm_read(buf, wg, streams, sink)
+            _, per = _events_time(lambda: swa.probe_hbm_read(buf, wg, streams, sink), reps, stream)
+            med = _stats(per)["median"]
+            gbs = nbytes / (med * 1e-3) / 1e9
+            if best is None or gbs > best["value"]:
+                best = {"value": gbs, "unit": "GB/s", "kernel": "probe_read_kernel (16-byte non-temporal loads)",
+                        "bytes": nbytes, "workgroups": wg, "streams": streams, "launch_ms_median": med}
+    del buf
+    torch.cuda.empty_cache()
+    MEASURED_PEAK["hbm"] = best
+    return MEASURED_PEAK
 
 
 def bench_prefill(name, steps, warmup, cold=False):
@@ -613,6 +669,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="time only the selected workload")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache prefill figure")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured MFMA and HBM peaks")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -630,6 +687,8 @@ def main():
         calibrate_copy(args.steps)
         return
 
+    if not args.no_peaks:
+        measured_peaks()
     extra = {}
     if not args.no_extras and args.workload == HEADLINE:
         # the other workloads first: the headline is timed last, on a chip
@@ -658,6 +717,8 @@ def main():
         "roofline": r["roofline"],
     }
     line["roofline"]["frac_str"] = f"{100 * r['roofline']['frac']:.1f}% of MI355X peak"
+    if MEASURED_PEAK:
+        line["measured_peak"] = MEASURED_PEAK
     if "cold_cache" in r:
         line["cold_cache"] = r["cold_cache"]
     if extra:

@@ -1,7 +1,8 @@
 """Exact causal sliding-window attention with attention sinks for AMD MI355X.
 
 The computation lives in libswa.so (hand-written HIP kernels for gfx950
-behind the C ABI of include/swa.h); this package is its thin Python binding.
+behind the C ABI of include/swa.h, with the measurement kernels of
+include/swa_probe.h); this package is its thin Python binding.
 
     from block_sparse_causal_band_amd import prefill, kv_append, decode
     from block_sparse_causal_band_amd import chunk_prefill, lse_merge
@@ -33,5 +34,7 @@ from .binding import (  # noqa: F401
     prefill,
     prefill_order,
     prefill_tile_shape,
+    probe_hbm_read,
+    probe_mfma_bf16,
     strerror,
 )

@@ -91,6 +91,12 @@ def lib() -> ctypes.CDLL:
         L.swa_prefill_tile_shape.restype = _int
         L.swa_prefill_order.argtypes = [_int, _int, _int, _vp, ctypes.c_long]
         L.swa_prefill_order.restype = ctypes.c_long
+        L.swa_probe_mfma_bf16.argtypes = [_vp, _int, _int, _vp]
+        L.swa_probe_mfma_bf16.restype = _int
+        L.swa_probe_mfma_bf16_flops.argtypes = [_int, _int]
+        L.swa_probe_mfma_bf16_flops.restype = ctypes.c_double
+        L.swa_probe_hbm_read.argtypes = [_vp, ctypes.c_size_t, _int, _int, _vp, _vp]
+        L.swa_probe_hbm_read.restype = _int
         _LIB = L
     return _LIB
 
@@ -467,3 +473,29 @@ def prefill_order(units: int, nqb: int, group: int = 1) -> np.ndarray:
     if got != total:
         raise SwaError(got, "swa_prefill_order")
     return out
+
+
+def probe_mfma_bf16(out, workgroups: int, iters: int) -> float:
+    """Enqueue the dense bf16 MFMA stream (measurement kernel) on out's
+    device; out: float32 [workgroups * 256].  Returns its FLOP count."""
+    _dev_tensor(out, "out")
+    _need(out.dtype.is_floating_point and out.element_size() == 4 and out.numel() >= workgroups * 256,
+          "out must be float32 with workgroups * 256 elements")
+    rc = lib().swa_probe_mfma_bf16(out.data_ptr(), int(workgroups), int(iters), _stream(out))
+    if rc != 0:
+        raise SwaError(rc, "swa_probe_mfma_bf16")
+    return float(lib().swa_probe_mfma_bf16_flops(int(workgroups), int(iters)))
+
+
+def probe_hbm_read(buf, workgroups: int, streams: int, sink) -> int:
+    """Enqueue the streaming read of buf (measurement kernel); sink: int32
+    [workgroups].  Returns the bytes read."""
+    _dev_tensor(buf, "buf")
+    _dev_tensor(sink, "sink")
+    _need(sink.element_size() == 4 and sink.numel() >= workgroups, "sink must hold workgroups 32-bit words")
+    nbytes = buf.numel() * buf.element_size()
+    rc = lib().swa_probe_hbm_read(buf.data_ptr(), nbytes, int(workgroups), int(streams), sink.data_ptr(),
+                                  _stream(buf))
+    if rc != 0:
+        raise SwaError(rc, "swa_probe_hbm_read")
+    return nbytes

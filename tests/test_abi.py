@@ -1,4 +1,4 @@
-"""libswa.so loads, exports every entry point of include/swa.h, and rejects
+"""libswa.so loads, exports every entry point that include/*.h declares, and rejects
 invalid arguments before launching anything.  CPU only: every call here
 fails validation, so no device work is enqueued."""
 import ctypes
@@ -10,16 +10,19 @@ import pytest
 import block_sparse_causal_band_amd as swa
 from block_sparse_causal_band_amd import binding
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "swa.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADERS = sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
 
 OK, EINVAL, EUNSUP, EALIGN, EHIP, EWS, ESCRATCH = 0, -1, -2, -3, -4, -5, -6
 P = 4096  # a fake, 16-byte aligned "device pointer": never dereferenced on these paths
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(swa_[a-z0-9_]+)\s*\(", src)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(swa_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
@@ -27,6 +30,22 @@ def test_header_declares_the_boundary():
     for want in ("swa_prefill_fwd", "swa_decode_fwd", "swa_kv_append", "swa_decode_workspace_bytes",
                  "swa_strerror", "swa_band_tiles"):
         assert want in names
+
+
+def test_headers_declare_the_measurement_probes():
+    assert {"swa_probe_mfma_bf16", "swa_probe_mfma_bf16_flops", "swa_probe_hbm_read"} <= set(declared_functions())
+
+
+def test_probe_rejects_and_counts():
+    L = swa.lib()
+    assert L.swa_probe_mfma_bf16(None, 1, 1, None) == EINVAL
+    assert L.swa_probe_mfma_bf16(P, 0, 1, None) == EINVAL
+    assert L.swa_probe_mfma_bf16(P + 2, 1, 1, None) == EALIGN
+    assert L.swa_probe_mfma_bf16_flops(3, 5) == 3 * 4 * 5 * 4 * 32768
+    assert L.swa_probe_mfma_bf16_flops(0, 5) == 0
+    assert L.swa_probe_hbm_read(P, 32768 * 4, 4, 3, P, None) == EINVAL       # streams
+    assert L.swa_probe_hbm_read(P, 32768 * 4 + 16, 4, 2, P, None) == EINVAL  # not whole rounds
+    assert L.swa_probe_hbm_read(P + 8, 32768 * 4, 4, 2, P, None) == EALIGN
 
 
 def test_library_exports_every_declared_symbol():
