@@ -351,20 +351,25 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
 
 // ---------------------------------------------------------------------------
 // Grouped-query decode on the matrix cores (bf16 q and cache).  The query
-// heads that share one key/value head are the 16-wide side of
-// v_mfma_f32_16x16x32_bf16 (heads past the group's are zero):
-//   S^T[16 keys x 16 heads] = K[16 keys x 32 d] Q^T    (D/32 MFMAs)
-//   O^T[16 d x 16 heads]   += V^T[16 d x 32 keys] P^T  (one per 16 columns of d)
+// heads that share one key/value head are the 16-wide side of the MFMAs
+// (heads past the group's are zero):
+//   S^T[16 keys x 16 heads] = K[16 keys x 32 d] Q^T  (v_mfma_f32_16x16x32_bf16, D/32 of them)
+//   O^T[16 d x 16 heads]   += V^T[16 d x 16 keys] P^T (v_mfma_f32_16x16x16_bf16, one per 16 columns)
 // so each cache row is read once for the whole group and the dot products
-// leave the VALU.  K fragments come straight from memory in the A-operand
-// layout (lane l: key l%16, d 8(l/16) .. +8 of a 32-wide step); V goes to
-// LDS by DMA (64-byte column blocks) and is read transposed with
-// ds_read_b64_tr_b16.  Lane l holds head l%16 in S^T, P^T and O^T alike, so a
-// head's softmax state sits in the 4 lanes l%16 = h and the accumulators need
-// no cross-lane traffic; the reference max moves lazily as in the prefill.
-// Each wave takes every 4th block of 32 cache rows of the workgroup's share,
-// one block ahead in flight; waves merge through LDS at the end.
-constexpr int kMfmaRows = 32;  // cache rows per block
+// leave the VALU.  Lane l holds head l%16 in S^T, P^T and O^T alike (the
+// score result is the probability operand as it stands), so a head's
+// softmax state sits in the 4 lanes l%16 = h and the accumulators need no
+// cross-lane traffic; the reference max moves lazily as in the prefill.
+// K and V of a block of 16 cache rows go to LDS by non-temporal DMA, each
+// load instruction moving 1 KB of whole rows, so the cache streams as a
+// plain sequential read (a non-temporal stream of half cache lines, as an
+// A-operand-shaped load from memory would be, reads every line twice); the
+// 16-byte chunks of each row are XOR-swizzled so that both the 16-byte K
+// operand reads (16 rows, one chunk) and the transposing V reads
+// (ds_read_b64_tr_b16: 8 keys, two chunks) hit distinct banks.  Each wave
+// takes every 4th block of the workgroup's share with the next block always
+// in flight (two stages); waves merge through LDS at the end.
+constexpr int kMfmaRows = 16;  // cache rows per block
 
 // Query heads per MFMA-decode workgroup: the largest divisor of the group
 // size that is at most 16.
@@ -381,9 +386,23 @@ typedef float mf32x4 __attribute__((ext_vector_type(4)));
 constexpr int vmcnt_only(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
 typedef short ms16x4 __attribute__((ext_vector_type(4)));
 
-// 16-byte buffer load of every lane into LDS at lds + 16 * lane (one wave).
-__device__ __forceinline__ void dma16_lds(__amdgpu_buffer_rsrc_t r, uint8_t *lds, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, 0, 0, 0);
+// 16-byte non-temporal buffer load of every lane into LDS at lds + 16 * lane
+// (one wave; aux 2 is the nt cache policy).
+__device__ __forceinline__ void dma16_lds_nt(__amdgpu_buffer_rsrc_t r, uint8_t *lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, 0, 0, 2);
+}
+
+// XOR swizzle of the 16-byte chunks of cache row r (of a 16-row block) in
+// LDS: chunk c sits at slot c ^ swz(r).  D = 128 (16 chunks of a 256-byte
+// row): a bijection on r, so 16 rows at one chunk fill all 64 banks, and the
+// 8 rows of a transposing read pass (r & 7) differ in the upper 3 bits of
+// the slot, so 8 rows x 2 adjacent chunks are 16 distinct slots.  D = 64
+// (8 chunks of a 128-byte row, two rows per 256 bytes): the same properties
+// within each row parity.
+template <int D>
+__device__ __forceinline__ int mfma_swz(int r) {
+    if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
+    else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
 }
 
 __device__ __forceinline__ ms16x4 lds_tr16(const uint8_t *p) {
@@ -407,16 +426,21 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
     const int64_t *__restrict__ pos, uint16_t *__restrict__ op, float *__restrict__ lsep, int heads, int kv_heads,
     int gw, int w, int g, float c2, float scale, float bias_raw, int splits, int rows_per_split,
     float *__restrict__ ws) {
-    constexpr int KS = D / 32;              // 32-wide d steps of the score product
-    constexpr int DB = D / 16;              // 16-wide column blocks of the output
+    constexpr int KS = D / 32;                          // 32-wide d steps of the score product
+    constexpr int DB = D / 16;                          // 16-wide column blocks of the output
     constexpr int kRowBytes = D * 2;
-    constexpr int kBlockBytes = kMfmaRows * kRowBytes;  // one V block in LDS
-    constexpr int kDma = kBlockBytes / 1024;            // 1 KB DMA loads per V block
+    constexpr int kBlockBytes = kMfmaRows * kRowBytes;  // K (or V) of one block
+    constexpr int kDma = kBlockBytes / 1024;            // 1 KB DMA loads per K (or V) block
     constexpr int kWaves = kDecThreads / 64;
-    // LDS: per wave two V blocks; reused for the cross-wave merge at the end
-    constexpr int kVBytes = kWaves * 2 * kBlockBytes;
+    // LDS: stage 0 of every wave in sbuf0, stage 1 in sbuf1 (two arrays, so
+    // that the compiler sees that the reads of one stage do not alias the DMA
+    // into the other and does not wait for that DMA before them); a stage of
+    // a wave is its block's K then V.  sbuf0 is reused for the merge.
+    constexpr int kStageBytes = 2 * kBlockBytes;
+    constexpr int kBufBytes = kWaves * kStageBytes;
     constexpr int kMergeBytes = kWaves * 16 * (D + 2) * 4;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[kVBytes > kMergeBytes ? kVBytes : kMergeBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t sbuf0[kBufBytes > kMergeBytes ? kBufBytes : kMergeBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t sbuf1[kBufBytes];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -434,8 +458,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
     const int64_t p = pos[b];
     const uint16_t *kc = kcp + (size_t)kvu * R * D;
     const uint16_t *vc = vcp + (size_t)kvu * R * D;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc, (uint32_t)R * kRowBytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc, (uint32_t)R * kRowBytes);
 
     // Q^T as the B operand: head hl, d 32 ks + 8 grp .. +8 (zero past the group)
     bf16x8 qf[KS];
@@ -455,19 +477,26 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
     const int r_end = min(R, r_begin + rows_per_split);
     const int nblk = (r_end - r_begin + kMfmaRows - 1) / kMfmaRows;
 
-    // V DMA: load i of a block fills LDS bytes [1 KB i, 1 KB (i+1)): column
-    // block c = byte / (32 * 64), key (byte % 2048) / 64, 16-byte piece.
-    uint32_t voffs[kDma];
+    // DMA load i of a block fills LDS bytes [1 KB i, 1 KB (i+1)) of its K (or
+    // V) area: row r = byte / kRowBytes, slot (byte % kRowBytes) / 16, which
+    // holds chunk slot ^ swz(r) of the row.
+    uint32_t doff[kDma];
 #pragma unroll
     for (int i = 0; i < kDma; ++i) {
         const int o = 1024 * i + 16 * lane;
-        const int cblk = o / (kMfmaRows * 64), key = (o % (kMfmaRows * 64)) / 64, piece = (o % 64) / 16;
-        voffs[i] = (uint32_t)key * kRowBytes + cblk * 64 + piece * 16;
+        const int r = o / kRowBytes, slot = (o % kRowBytes) / 16;
+        doff[i] = (uint32_t)(r * kRowBytes + 16 * (slot ^ mfma_swz<D>(r)));
     }
-    uint8_t *vb0 = smem + wave * 2 * kBlockBytes;
-    // transposed V read: lane j of group grp supplies key (row) j/4 of the
-    // group's 4 keys and the 8-byte piece of columns 4 (j%4) .. +3
-    const uint32_t vrd = (uint32_t)((hl >> 2) * 64 + 8 * (hl & 3));
+    // K operand read (16 bytes): key hl, chunk 4 ks + grp
+    const int swz_k = mfma_swz<D>(hl);
+    // transposed V read: lane j of group grp supplies key 4 grp + j/4 and the
+    // 8-byte piece of columns 16 db + 4 (j%4) .. +3, which is half (j%4)&1 of
+    // chunk 2 db + (j%4)/2; the instruction hands lane j of the group column
+    // 16 db + j of the group's four keys
+    const int vr = 4 * grp + (hl >> 2);
+    const int swz_v = mfma_swz<D>(vr);
+    const uint32_t vrow = (uint32_t)(vr * kRowBytes + 8 * (hl & 1));
+    const int vchunk = (hl >> 1) & 1;
 
     mf32x4 oacc[DB];
 #pragma unroll
@@ -475,59 +504,58 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
     float m_run = kNegInf, negm = 0.f, l_run = 0.f;
     const float tau = 8.f / c2;
 
-    // K fragments of one block: [16-key half][d step]
-    auto load_k = [&](int blk, bf16x8 (&kx)[2][KS]) {
-        const int row0 = r_begin + blk * kMfmaRows;
+    // First cache row of block blk of this wave's share; a block past the
+    // share starts at row R, past the buffer range, so its loads read zeros
+    // and move no memory (the prefetch below is issued unconditionally: no
+    // branch around it, hence no point where the compiler must assume either
+    // history and wait for every load in flight).
+    auto block_row = [&](int blk) -> int { return (blk < nblk) ? r_begin + blk * kMfmaRows : R; };
+    auto stage = [&](int st) -> uint8_t * { return (st ? sbuf1 : sbuf0) + wave * kStageBytes; };
+    auto load = [&](int blk, int st) {
+        const int row0 = block_row(blk);
+        const uint32_t range = (uint32_t)(R - row0) * kRowBytes;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + (size_t)row0 * D, range);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + (size_t)row0 * D, range);
+        uint8_t *dst = stage(st);
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int i = 0; i < kDma; ++i) dma16_lds_nt(rk, dst + 1024 * i, doff[i]);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                kx[rb][ks] = __builtin_bit_cast(
-                    bf16x8, buffer_load16(rk, (uint32_t)(row0 + 16 * rb + hl) * kRowBytes + (32 * ks + 8 * grp) * 2));
-    };
-    auto load_v = [&](int blk, int buf) {
-        const int row0 = r_begin + blk * kMfmaRows;
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(vc + (size_t)row0 * D, (uint32_t)(R - row0) * kRowBytes);
-#pragma unroll
-        for (int i = 0; i < kDma; ++i) dma16_lds(r, vb0 + buf * kBlockBytes + 1024 * i, voffs[i]);
+        for (int i = 0; i < kDma; ++i) dma16_lds_nt(rv, dst + kBlockBytes + 1024 * i, doff[i]);
     };
     // one block: scores, mask, softmax, O^T += V^T P^T
-    auto compute = [&](int blk, int buf, const bf16x8 (&kx)[2][KS]) {
+    auto compute = [&](int blk, int st) {
         const int row0 = r_begin + blk * kMfmaRows;
-        mf32x4 s[2];
+        const uint8_t *kb = stage(st);
+        const uint8_t *vb = kb + kBlockBytes;
+        mf32x4 sc = mf32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            s[rb] = mf32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx[rb][ks], qf[ks], s[rb], 0, 0, 0);
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kb + hl * kRowBytes + 16 * ((4 * ks + grp) ^ swz_k));
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], sc, 0, 0, 0);
         }
-        // lane (hl, grp) holds keys 16 rb + 4 grp + i of the block: which
-        // position each row holds and whether it is read (as in decode_kernel)
+        // lane (hl, grp) holds keys 4 grp + i of the block: which position
+        // each row holds and whether it is read (as in decode_kernel)
         float mx = kNegInf;
-        uint32_t vkeep[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};  // per 2 key slots
+        uint32_t vkeep[2] = {0xffffffffu, 0xffffffffu};  // per 2 key slots
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = row0 + 16 * rb + 4 * grp + i;
-                const int sl = r - g;
-                int dd = pm - sl;
-                dd += (dd < 0) ? w : 0;
-                const int64_t t = (r < g) ? (int64_t)r : (ring_full ? p - dd : (int64_t)sl);
-                const bool v_sink = ((int64_t)r <= p) && ((int64_t)r < win_lo);
-                const bool v_ring = ring_full || ((int64_t)sl <= p);
-                const bool valid = (r < r_end) && (p >= 0) && ((r < g) ? v_sink : v_ring);
-                const float x = s[rb][i] + ((t < g) ? bias_raw : 0.f);
-                s[rb][i] = valid ? x : kNegInf;
-                mx = fmaxf(mx, s[rb][i]);
-                const int e = 4 * rb + i;  // key slot of this row in the P and V^T operands
-                if (!valid) vkeep[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-            }
+        for (int i = 0; i < 4; ++i) {
+            const int r = row0 + 4 * grp + i;
+            const int sl = r - g;
+            int dd = pm - sl;
+            dd += (dd < 0) ? w : 0;
+            const int64_t t = (r < g) ? (int64_t)r : (ring_full ? p - dd : (int64_t)sl);
+            const bool v_sink = ((int64_t)r <= p) && ((int64_t)r < win_lo);
+            const bool v_ring = ring_full || ((int64_t)sl <= p);
+            const bool valid = (r < r_end) && (p >= 0) && ((r < g) ? v_sink : v_ring);
+            const float x = sc[i] + ((t < g) ? bias_raw : 0.f);
+            sc[i] = valid ? x : kNegInf;
+            mx = fmaxf(mx, sc[i]);
+            if (!valid) vkeep[i >> 1] &= (i & 1) ? 0x0000ffffu : 0xffff0000u;
+        }
         // a row that is not read may hold anything (an unwritten slot): its
         // P is 0 and, where such rows occur, its V values are zeroed too, so
         // that 0 * NaN cannot reach the output
-        const bool any_unread = __any((vkeep[0] & vkeep[1] & vkeep[2] & vkeep[3]) != 0xffffffffu);
+        const bool any_unread = __any((vkeep[0] & vkeep[1]) != 0xffffffffu);
         mx = half_swap_max(quarter_swap_max(mx));  // over the head's 4 lanes
         if (__any(mx > m_run + tau)) {
             const float m_new = fmaxf(m_run, mx);
@@ -538,70 +566,59 @@ __global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
 #pragma unroll
             for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
         }
-        // P^T as the B operand: keys 4 grp + i of half 0, then of half 1
-        bf16x8 pk;
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pk[4 * rb + i] = static_cast<__bf16>(fast_exp2(fmaf(s[rb][i], c2, negm)));
+        // P^T as the B operand: keys 4 grp + i
+        const bf16x2 p01 = {static_cast<__bf16>(fast_exp2(fmaf(sc[0], c2, negm))),
+                            static_cast<__bf16>(fast_exp2(fmaf(sc[1], c2, negm)))};
+        const bf16x2 p23 = {static_cast<__bf16>(fast_exp2(fmaf(sc[2], c2, negm))),
+                            static_cast<__bf16>(fast_exp2(fmaf(sc[3], c2, negm)))};
         {
             const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
-            const bf16x2 p01 = {pk[0], pk[1]}, p23 = {pk[2], pk[3]}, p45 = {pk[4], pk[5]}, p67 = {pk[6], pk[7]};
-            float ls = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, 0.f, false);
-            ls = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, ls, false);
-            ls = __builtin_amdgcn_fdot2_f32_bf16(p45, ones, ls, false);
-            l_run += __builtin_amdgcn_fdot2_f32_bf16(p67, ones, ls, false);
+            const float ls = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, 0.f, false);
+            l_run += __builtin_amdgcn_fdot2_f32_bf16(p23, ones, ls, false);
         }
-        const uint8_t *vb = vb0 + buf * kBlockBytes;
+        const ms16x4 pk = __builtin_bit_cast(
+            ms16x4, make_uint2(__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)));
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const uint8_t *base = vb + (db >> 1) * (kMfmaRows * 64) + 32 * (db & 1) + vrd;
-            const ms16x4 lo = lds_tr16(base + (4 * grp) * 64);
-            const ms16x4 hi = lds_tr16(base + (16 + 4 * grp) * 64);
-            bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            ms16x4 vf = lds_tr16(vb + vrow + 16 * ((2 * db + vchunk) ^ swz_v));
             if (any_unread) {
-                u32x4 u = __builtin_bit_cast(u32x4, vf);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) u[j] &= vkeep[j];
-                vf = __builtin_bit_cast(bf16x8, u);
+                uint2 u = __builtin_bit_cast(uint2, vf);
+                u.x &= vkeep[0];
+                u.y &= vkeep[1];
+                vf = __builtin_bit_cast(ms16x4, u);
             }
-            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pk, oacc[db], 0, 0, 0);
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pk, oacc[db], 0, 0, 0);
         }
     };
 
-    // this wave's blocks wave, wave + 4, ...: two in flight, buffers 0 and 1
-    // alternating (the loop is unrolled by two so that each has fixed registers)
+    // this wave's blocks wave, wave + 4, ...: the next one always in flight
+    // while one is computed, stages 0 and 1 alternating (the loop is
+    // unrolled by two so that each stage is named statically)
     const int my_blocks = (nblk > wave) ? (nblk - wave + kWaves - 1) / kWaves : 0;
-    bf16x8 ka[2][KS], kb[2][KS];
     if (my_blocks > 0) {
-        load_k(wave, ka);
-        load_v(wave, 0);
-    }
-    for (int it = 0; it < my_blocks; it += 2) {
-        const int blk = wave + it * kWaves;
-        if (it + 1 < my_blocks) {
-            load_k(blk + kWaves, kb);
-            load_v(blk + kWaves, 1);
-            __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * KS + kDma));  // block it has landed
-        } else {
-            __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+        load(wave, 0);
+        // (sched_barrier: the next block's loads all issue before the wait)
+        for (int it = 0;; it += 2) {
+            const int blk = wave + it * kWaves;
+            load(blk + kWaves, 1);  // an empty block past the share's end
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kDma));  // block it has landed
+            compute(blk, 0);
+            if (it + 1 >= my_blocks) break;
+            load(blk + 2 * kWaves, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kDma));  // block it + 1 has landed
+            compute(blk + kWaves, 1);
+            if (it + 2 >= my_blocks) break;
         }
-        compute(blk, 0, ka);
-        if (it + 1 >= my_blocks) break;
-        if (it + 2 < my_blocks) {
-            load_k(blk + 2 * kWaves, ka);
-            load_v(blk + 2 * kWaves, 0);
-            __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * KS + kDma));  // block it + 1 has landed
-        } else {
-            __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
-        }
-        compute(blk + kWaves, 1, kb);
     }
+    // the last prefetch (an empty block) writes LDS: done before the merge reuses it
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
 
     // ---- merge the waves: per head h, (m, l, o[D]) of each wave ----
     const float l_head = half_swap_sum(quarter_swap_sum(l_run));
-    __syncthreads();  // every wave is done with its V blocks
-    float *sm = reinterpret_cast<float *>(smem);  // [wave][head][D + 2]: o[D], m, l
+    __syncthreads();  // every wave is done with its stages
+    float *sm = reinterpret_cast<float *>(sbuf0);  // [wave][head][D + 2]: o[D], m, l
     {
         float *rec = sm + (wave * 16 + hl) * (D + 2);
 #pragma unroll
