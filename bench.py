@@ -95,16 +95,16 @@ PATTERN = {
 # the source has changed since, the figure no longer describes the kernel and
 # `traffic` is reported as null.
 MEASURED_TRAFFIC = {
-    "sink_prefill": {"bytes": 1074245697, "source_digest": "79a1d31e79b97b17"},
-    "mistral_prefill": {"bytes": 537759176, "source_digest": "79a1d31e79b97b17"},
-    "gemma3_local_prefill": {"bytes": 2213233591, "source_digest": "79a1d31e79b97b17"},
-    "gqa_prefill": {"bytes": 336036239, "source_digest": "79a1d31e79b97b17"},
-    "chunk_prefill": {"bytes": 117720138, "source_digest": "79a1d31e79b97b17"},
-    "dilated_prefill": {"bytes": 541697007, "source_digest": "79a1d31e79b97b17"},
-    "landmark_prefill": {"bytes": 948370776, "source_digest": "79a1d31e79b97b17"},
-    "rolling_decode": {"bytes": 4300158521, "source_digest": "be64c163c11ea9c2"},
-    "gqa_decode": {"bytes": 1076026282, "source_digest": "be64c163c11ea9c2"},
-    "fp8_decode": {"bytes": 2150936125, "source_digest": "be64c163c11ea9c2"},
+    "sink_prefill": {"bytes": 1074195474, "source_digest": "95c7b2c8028b18ae"},
+    "mistral_prefill": {"bytes": 537798253, "source_digest": "95c7b2c8028b18ae"},
+    "gemma3_local_prefill": {"bytes": 2218407186, "source_digest": "95c7b2c8028b18ae"},
+    "gqa_prefill": {"bytes": 336031775, "source_digest": "95c7b2c8028b18ae"},
+    "chunk_prefill": {"bytes": 117518105, "source_digest": "95c7b2c8028b18ae"},
+    "dilated_prefill": {"bytes": 542189568, "source_digest": "95c7b2c8028b18ae"},
+    "landmark_prefill": {"bytes": 553672300, "source_digest": "95c7b2c8028b18ae"},
+    "rolling_decode": {"bytes": 4300158266, "source_digest": "b63b9c70bf96ac2b"},
+    "gqa_decode": {"bytes": 1075968367, "source_digest": "b63b9c70bf96ac2b"},
+    "fp8_decode": {"bytes": 2150923135, "source_digest": "b63b9c70bf96ac2b"},
 }
 # Matrix-core figures of the prefill kernels from rocprofv3 counter runs
 # (SQ_INSTS_MFMA, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, SQ_BUSY_CYCLES per
@@ -114,16 +114,20 @@ MEASURED_TRAFFIC = {
 #   mfma_busy_per_simd: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs);
 #   clock_ghz: GRBM_GUI_ACTIVE / 8 XCDs / kernel duration.
 MEASURED_COUNTERS = {
-    "sink_prefill": {"issued_per_band": 1.0448, "mfma_busy_per_simd": 0.5903, "clock_ghz": 1.823,
-                     "valu_per_mfma": 4.78, "source_digest": "79a1d31e79b97b17"},
-    "mistral_prefill": {"issued_per_band": 1.0312, "mfma_busy_per_simd": 0.5611, "clock_ghz": 1.867,
-                        "valu_per_mfma": 4.72, "source_digest": "79a1d31e79b97b17"},
-    "gemma3_local_prefill": {"issued_per_band": 1.125, "mfma_busy_per_simd": 0.4904, "clock_ghz": 1.91,
-                             "valu_per_mfma": 5.97, "source_digest": "79a1d31e79b97b17"},
-    "gqa_prefill": {"issued_per_band": 1.0312, "mfma_busy_per_simd": 0.5728, "clock_ghz": 1.852,
-                    "valu_per_mfma": 4.72, "source_digest": "79a1d31e79b97b17"},
-    "chunk_prefill": {"issued_per_band": 1.0537, "mfma_busy_per_simd": 0.5568, "clock_ghz": 1.846,
-                      "valu_per_mfma": 4.9, "source_digest": "79a1d31e79b97b17"},
+    "sink_prefill": {"issued_per_band": 1.0448, "mfma_busy_per_simd": 0.6027, "clock_ghz": 1.783,
+                     "valu_per_mfma": 4.78, "source_digest": "95c7b2c8028b18ae"},
+    "mistral_prefill": {"issued_per_band": 1.0312, "mfma_busy_per_simd": 0.575, "clock_ghz": 1.821,
+                        "valu_per_mfma": 4.72, "source_digest": "95c7b2c8028b18ae"},
+    "gemma3_local_prefill": {"issued_per_band": 1.125, "mfma_busy_per_simd": 0.4965, "clock_ghz": 1.894,
+                             "valu_per_mfma": 5.97, "source_digest": "95c7b2c8028b18ae"},
+    "gqa_prefill": {"issued_per_band": 1.0312, "mfma_busy_per_simd": 0.5921, "clock_ghz": 1.796,
+                    "valu_per_mfma": 4.72, "source_digest": "95c7b2c8028b18ae"},
+    "chunk_prefill": {"issued_per_band": 1.0537, "mfma_busy_per_simd": 0.5592, "clock_ghz": 1.824,
+                      "valu_per_mfma": 4.9, "source_digest": "95c7b2c8028b18ae"},
+    "dilated_prefill": {"issued_per_band": 1.1248, "mfma_busy_per_simd": 0.4334, "clock_ghz": 2.054,
+                        "valu_per_mfma": 6.22, "source_digest": "95c7b2c8028b18ae"},
+    "landmark_prefill": {"issued_per_band": 1.0494, "mfma_busy_per_simd": 0.5587, "clock_ghz": 1.851,
+                         "valu_per_mfma": 5.01, "source_digest": "95c7b2c8028b18ae"},
 }
 CSRC = os.path.join(ROOT, "block_sparse_causal_band_amd", "csrc")
 
@@ -446,9 +450,10 @@ def bench_pattern(name, steps, warmup):
         "dtype": "bf16",
         "config": {"workload": name, "batch": B, "heads": H, "n": n, "d": d, "pattern": kind, "w": w, "g": g,
                    "r": r, "sink_bias": beta, "band_flops_per_step": flops},
-        "roofline": _roofline("mfma", flops, per, PEAK_BF16_TFLOPS, "TFLOP/s", None,
+        "roofline": _roofline("mfma", flops, per, PEAK_BF16_TFLOPS, "TFLOP/s", measured_traffic(name, "prefill.hip"),
                               ("prefill_bf16_kernel<128,strided> (dilated classes)" if kind == "dilated" else
-                               "prefill_bf16_kernel<128,landmark> (landmark tiles, then window and sink tiles, one launch)")),
+                               "prefill_bf16_kernel<128,landmark> (landmark tiles, then window and sink tiles, one launch)"),
+                              measured_counters(name)),
     }
 
 
