@@ -11,12 +11,15 @@ resident in HBM.  `value` is band-TFLOP/s: 4*d FLOP per attended (query,
 key) pair (two products, a multiply-add counted as 2), pairs counted exactly
 per row.
 
-The same line carries, under "extra", the Mistral-shaped prefill (n=16384,
-w=4096), the Gemma-3-style local prefill (16 heads, n=131072, w=1024), the
-Mistral-shaped grouped-query prefill (32 query heads over 8 key/value heads), the
-rolling-cache decode (batch 64, 32 heads, w=4096, g=4, positions in [4096,
-131072]; KV GB/s) and that decode step's one-token kv_append, each with its
-own roofline.  They run before the headline, which is timed last.
+The same line carries, under "extra", every other workload, each with its
+own roofline: the rolling-cache decode (batch 64, 32 heads, w=4096, g=4,
+positions in [4096, 131072]; KV GB/s), its grouped-query (8 key/value heads)
+and FP8-cache forms, the Mistral-shaped prefill (n=16384, w=4096), the
+Gemma-3-style local prefill (16 heads, n=131072, w=1024), the Mistral-shaped
+grouped-query prefill (32 query heads over 8 key/value heads), the chunked
+prefill against the cache, the dilated and the landmark prefills, and the
+decode step's one-token kv_append.  They run before the headline, which is
+timed last.
 
 Timing: every launch is bracketed by HIP events on the stream the kernel
 runs on; `ms_per_step` is the whole timed region over K steps, `roofline`
@@ -698,7 +701,8 @@ def main():
     if not args.no_extras and args.workload == HEADLINE:
         # the other workloads first: the headline is timed last, on a chip
         # whose clock has settled under load
-        for name in ("rolling_decode", "mistral_prefill", "gemma3_local_prefill", "gqa_prefill"):
+        for name in ("rolling_decode", "gqa_decode", "fp8_decode", "mistral_prefill", "gemma3_local_prefill",
+                     "gqa_prefill", "chunk_prefill", "dilated_prefill", "landmark_prefill"):
             extra[name] = _brief(_bench(name, args.steps, args.warmup))
             torch.cuda.empty_cache()
         extra["kv_append"] = _brief(bench_kv_append("rolling_decode", args.steps, args.warmup))
