@@ -98,13 +98,13 @@ PATTERN = {
 # the source has changed since, the figure no longer describes the kernel and
 # `traffic` is reported as null.
 MEASURED_TRAFFIC = {
-    "sink_prefill": {"bytes": 1074195474, "source_digest": "95c7b2c8028b18ae"},
-    "mistral_prefill": {"bytes": 537798253, "source_digest": "95c7b2c8028b18ae"},
-    "gemma3_local_prefill": {"bytes": 2218407186, "source_digest": "95c7b2c8028b18ae"},
-    "gqa_prefill": {"bytes": 336031775, "source_digest": "95c7b2c8028b18ae"},
-    "chunk_prefill": {"bytes": 117518105, "source_digest": "95c7b2c8028b18ae"},
-    "dilated_prefill": {"bytes": 542189568, "source_digest": "95c7b2c8028b18ae"},
-    "landmark_prefill": {"bytes": 553672300, "source_digest": "95c7b2c8028b18ae"},
+    "sink_prefill": {"bytes": 1074172356, "source_digest": "aafd3b00c1b0755b"},
+    "mistral_prefill": {"bytes": 537736873, "source_digest": "aafd3b00c1b0755b"},
+    "gemma3_local_prefill": {"bytes": 2192468673, "source_digest": "aafd3b00c1b0755b"},
+    "gqa_prefill": {"bytes": 336029864, "source_digest": "aafd3b00c1b0755b"},
+    "chunk_prefill": {"bytes": 117737531, "source_digest": "aafd3b00c1b0755b"},
+    "dilated_prefill": {"bytes": 541765770, "source_digest": "aafd3b00c1b0755b"},
+    "landmark_prefill": {"bytes": 553675195, "source_digest": "aafd3b00c1b0755b"},
     "rolling_decode": {"bytes": 4300158266, "source_digest": "b63b9c70bf96ac2b"},
     "gqa_decode": {"bytes": 1075968367, "source_digest": "b63b9c70bf96ac2b"},
     "fp8_decode": {"bytes": 2150923135, "source_digest": "b63b9c70bf96ac2b"},
@@ -117,20 +117,20 @@ MEASURED_TRAFFIC = {
 #   mfma_busy_per_simd: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs);
 #   clock_ghz: GRBM_GUI_ACTIVE / 8 XCDs / kernel duration.
 MEASURED_COUNTERS = {
-    "sink_prefill": {"issued_per_band": 1.0448, "mfma_busy_per_simd": 0.6027, "clock_ghz": 1.783,
-                     "valu_per_mfma": 4.78, "source_digest": "95c7b2c8028b18ae"},
-    "mistral_prefill": {"issued_per_band": 1.0312, "mfma_busy_per_simd": 0.575, "clock_ghz": 1.821,
-                        "valu_per_mfma": 4.72, "source_digest": "95c7b2c8028b18ae"},
-    "gemma3_local_prefill": {"issued_per_band": 1.125, "mfma_busy_per_simd": 0.4965, "clock_ghz": 1.894,
-                             "valu_per_mfma": 5.97, "source_digest": "95c7b2c8028b18ae"},
-    "gqa_prefill": {"issued_per_band": 1.0312, "mfma_busy_per_simd": 0.5921, "clock_ghz": 1.796,
-                    "valu_per_mfma": 4.72, "source_digest": "95c7b2c8028b18ae"},
-    "chunk_prefill": {"issued_per_band": 1.0537, "mfma_busy_per_simd": 0.5592, "clock_ghz": 1.824,
-                      "valu_per_mfma": 4.9, "source_digest": "95c7b2c8028b18ae"},
-    "dilated_prefill": {"issued_per_band": 1.1248, "mfma_busy_per_simd": 0.4334, "clock_ghz": 2.054,
-                        "valu_per_mfma": 6.22, "source_digest": "95c7b2c8028b18ae"},
-    "landmark_prefill": {"issued_per_band": 1.0494, "mfma_busy_per_simd": 0.5587, "clock_ghz": 1.851,
-                         "valu_per_mfma": 5.01, "source_digest": "95c7b2c8028b18ae"},
+    "sink_prefill": {"issued_per_band": 1.0448, "mfma_busy_per_simd": 0.5984, "clock_ghz": 1.809,
+                     "valu_per_mfma": 4.78, "source_digest": "aafd3b00c1b0755b"},
+    "mistral_prefill": {"issued_per_band": 1.0312, "mfma_busy_per_simd": 0.5748, "clock_ghz": 1.867,
+                        "valu_per_mfma": 4.72, "source_digest": "aafd3b00c1b0755b"},
+    "gemma3_local_prefill": {"issued_per_band": 1.125, "mfma_busy_per_simd": 0.4951, "clock_ghz": 1.938,
+                             "valu_per_mfma": 5.97, "source_digest": "aafd3b00c1b0755b"},
+    "gqa_prefill": {"issued_per_band": 1.0312, "mfma_busy_per_simd": 0.5904, "clock_ghz": 1.844,
+                    "valu_per_mfma": 4.72, "source_digest": "aafd3b00c1b0755b"},
+    "chunk_prefill": {"issued_per_band": 1.0537, "mfma_busy_per_simd": 0.5658, "clock_ghz": 1.856,
+                      "valu_per_mfma": 4.9, "source_digest": "aafd3b00c1b0755b"},
+    "dilated_prefill": {"issued_per_band": 1.1248, "mfma_busy_per_simd": 0.43, "clock_ghz": 2.118,
+                        "valu_per_mfma": 6.22, "source_digest": "aafd3b00c1b0755b"},
+    "landmark_prefill": {"issued_per_band": 1.0494, "mfma_busy_per_simd": 0.5562, "clock_ghz": 1.89,
+                         "valu_per_mfma": 5.01, "source_digest": "aafd3b00c1b0755b"},
 }
 CSRC = os.path.join(ROOT, "block_sparse_causal_band_amd", "csrc")
 

@@ -64,6 +64,27 @@ int check_dtype_d(swa_dtype_t dtype, int d) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_EHIP; }
 
+// Whether a prefill grid of units x query blocks fits in INT_MAX workgroups
+// (each product checked before it is formed: batch x heads alone can pass
+// 2^62).
+bool prefill_grid_fits(int batch, int heads, int units_mul, long long nqb) {
+    long long units = (long long)batch * heads;  // < 2^62
+    if (units > INT_MAX / units_mul) return false;
+    units *= units_mul;
+    return units <= INT_MAX / nqb;
+}
+
+// Whether the append grid (one thread per 16-byte chunk of each appended row,
+// 256 threads per workgroup) fits in INT_MAX workgroups: batch x heads x
+// tokens x chunks, each product checked before it is formed.
+bool append_grid_fits(int batch, int heads, int t_new, int chunks_per_row) {
+    const long long limit = (long long)INT_MAX * 256;  // chunks that INT_MAX workgroups cover
+    long long chunks = (long long)batch * heads;        // < 2^62
+    if (chunks > limit / t_new) return false;
+    chunks *= t_new;
+    return chunks <= limit / chunks_per_row;
+}
+
 }  // namespace
 
 extern "C" {
@@ -86,15 +107,14 @@ int swa_prefill_fwd_gqa(const void *q, const void *k, const void *v, void *o, fl
                         hipStream_t stream) {
     if (!q || !k || !v || !o) return SWA_EINVAL;
     if (batch < 1 || heads < 1 || n < 1 || w < 1 || g < 0) return SWA_EINVAL;
+    if (g > n) g = n;  // every position a sink either way (and the tile arithmetic stays in int)
     if (kv_heads < 1 || kv_heads > heads || heads % kv_heads != 0) return SWA_EINVAL;
     if (!std::isfinite(scale) || !(scale > 0.f) || !std::isfinite(sink_bias)) return SWA_EINVAL;
     int st = check_dtype_d(dtype, d);
     if (st != SWA_OK) return st;
     const int bq = swa::prefill_bq(dtype == SWA_BF16);
     if (n > INT_MAX - bq) return SWA_EINVAL;
-    const long long units = (long long)batch * heads;
-    const long long nqb = (n + bq - 1) / bq;
-    if (units * nqb > INT_MAX) return SWA_EINVAL;
+    if (!prefill_grid_fits(batch, heads, 1, (n + bq - 1) / bq)) return SWA_EINVAL;
     // byte offsets within one (batch, head)'s rows stay below 2^32 for the buffer loads
     if ((long long)n * d * (dtype == SWA_BF16 ? 2 : 4) >= (1LL << 32)) return SWA_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned4(lse)))
@@ -119,8 +139,7 @@ int swa_kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v
         (reinterpret_cast<uintptr_t>(pos) & 7u))
         return SWA_EALIGN;
     if (t_new == 0) return SWA_OK;
-    const long long blocks = ((long long)batch * heads * t_new * (d * (dtype == SWA_BF16 ? 2 : 4) / 16) + 255) / 256;
-    if (blocks > INT_MAX) return SWA_EINVAL;
+    if (!append_grid_fits(batch, heads, t_new, d * (dtype == SWA_BF16 ? 2 : 4) / 16)) return SWA_EINVAL;
     return status_of(swa::launch_kv_append(k_cache, v_cache, k_new, v_new, pos, batch, heads, t_new, d, w, g,
                                            dtype == SWA_BF16, stream));
 }
@@ -137,9 +156,7 @@ static int check_prefill(const void *q, const void *k, const void *v, const void
     if (st != SWA_OK) return st;
     const int bq = swa::prefill_bq(dtype == SWA_BF16);
     if (n > INT_MAX - bq) return SWA_EINVAL;
-    const long long units = (long long)batch * heads * units_mul;
-    const long long nqb = (n + bq - 1) / bq;
-    if (units * nqb > INT_MAX) return SWA_EINVAL;
+    if (!prefill_grid_fits(batch, heads, units_mul, (n + bq - 1) / bq)) return SWA_EINVAL;
     const long long row_bytes = (long long)d * (dtype == SWA_BF16 ? 2 : 4);
     if ((long long)n * row_bytes >= (1LL << 32)) return SWA_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned4(lse)))
@@ -175,6 +192,7 @@ int swa_landmark_prefill_fwd(const void *q, const void *k, const void *v, void *
     if (n >= 1 && r > n) r = n;  // every stride >= n has the one landmark 0
     int st = check_prefill(q, k, v, o, lse, batch, heads, kv_heads, n, d, w, g, scale, sink_bias, dtype, 1);
     if (st != SWA_OK) return st;
+    if (g > n) g = n;  // every position a sink (and no landmark) either way
     const size_t need = swa_landmark_workspace_bytes(batch, heads, n, d, dtype);
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return SWA_EWORKSPACE;
@@ -213,9 +231,7 @@ int swa_chunk_prefill_fwd(const void *q, const void *k_new, const void *v_new, c
     if (st != SWA_OK) return st;
     const int bq = swa::prefill_bq(dtype == SWA_BF16);
     if (t > INT_MAX - bq) return SWA_EINVAL;
-    const long long units = (long long)batch * heads;
-    const long long nqb = (t + bq - 1) / bq;
-    if (units * nqb > INT_MAX) return SWA_EINVAL;
+    if (!prefill_grid_fits(batch, heads, 1, (t + bq - 1) / bq)) return SWA_EINVAL;
     // byte offsets of one (batch, head)'s rows stay below 2^32 for the buffer loads
     const long long row_bytes = (long long)d * (dtype == SWA_BF16 ? 2 : 4);
     if ((long long)t * row_bytes >= (1LL << 32) || ((long long)g + w) * row_bytes >= (1LL << 32)) return SWA_EINVAL;
@@ -233,7 +249,9 @@ int swa_lse_merge(const void *o_a, const float *lse_a, const void *o_b, const fl
     if (rows < 1) return SWA_EINVAL;
     int st = check_dtype_d(dtype, d);
     if (st != SWA_OK) return st;
-    if (rows * (d / 4) / 256 + 1 > INT_MAX) return SWA_EINVAL;
+    // one thread per 4 columns of a row, 256 per workgroup: at most INT_MAX - 1
+    // workgroups (rows x (d/4) is not formed: rows can be near LLONG_MAX)
+    if (rows > ((long long)INT_MAX - 1) * 256 / (d / 4)) return SWA_EINVAL;
     if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o) || !aligned4(lse_a) || !aligned4(lse_b) ||
         (lse && !aligned4(lse)))
         return SWA_EALIGN;
@@ -252,8 +270,7 @@ int swa_kv_append_fp8(void *k_cache, void *v_cache, const void *k_new, const voi
         (reinterpret_cast<uintptr_t>(pos) & 7u) || !aligned4(k_scale) || !aligned4(v_scale))
         return SWA_EALIGN;
     if (t_new == 0) return SWA_OK;
-    const long long blocks = ((long long)batch * heads * t_new * (d / 8) + 255) / 256;
-    if (blocks > INT_MAX) return SWA_EINVAL;
+    if (!append_grid_fits(batch, heads, t_new, d / 8)) return SWA_EINVAL;
     return status_of(swa::launch_kv_append_fp8(k_cache, v_cache, k_new, v_new, pos, k_scale, v_scale, batch, heads,
                                                t_new, d, w, g, dtype == SWA_BF16, stream));
 }
@@ -355,6 +372,9 @@ int swa_decode_fwd(const void *q, const void *k_cache, const void *v_cache, cons
 
 long swa_band_tiles(int n, int w, int g, int bq, int bk, int *out, long cap) {
     if (n < 1 || w < 1 || g < 0 || bq < 1 || bk < 1 || cap < 0 || (cap > 0 && !out)) return SWA_EINVAL;
+    // the block and tile arithmetic (q0 + bq, the last key of a tile) stays within int
+    if (n > INT_MAX - bq || n > INT_MAX - bk) return SWA_EINVAL;
+    if (g > n) g = n;  // the same tiles and FULL tests (every position a sink)
     long count = 0;
     const int nqb = (n + bq - 1) / bq;
     for (int qb = 0; qb < nqb; ++qb) {

@@ -117,6 +117,10 @@ struct PathArgs {
     int mode;              // strided: 1 dilated, 2 landmark part
 };
 constexpr int kNoWindow = 1 << 30;  // a window wider than any sequence
+// Chunk positions are accepted while pos + t stays this far below INT_MAX, so
+// that every position sum of the tile arithmetic (a block's last row, a
+// tile's last key, the next tile's first) is an int.
+constexpr int kPosHeadroom = 1024;
 
 // Byte offset of row `row` of a buffer of n rows, the row index formed in 64
 // bits and clamped to n: a row at or past n reads as zero through the buffer
@@ -344,7 +348,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     if constexpr (CHUNK) {
         const int b = unit / heads;
         const int64_t pb = ca.pos[b];
-        if (pb < 0 || pb > (int64_t)(0x7fffffff - n)) {
+        if (pb < 0 || pb > (int64_t)(0x7fffffff - kPosHeadroom - n)) {
             // no valid position: the rows are NaN
             if (qi < n) {
                 uint16_t *orow = op + base + (size_t)qi * D;
@@ -853,7 +857,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(
     if constexpr (CHUNK) {
         const int b = unit / heads;
         const int64_t pb = ca.pos[b];
-        if (pb < 0 || pb > (int64_t)(0x7fffffff - n)) {
+        if (pb < 0 || pb > (int64_t)(0x7fffffff - kPosHeadroom - n)) {
             if (qi < n) {
                 float *orow = op + base + (size_t)qi * D;
                 for (int c = 4 * lh; c < D; c += 8) {

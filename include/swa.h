@@ -73,7 +73,8 @@ enum {
  *   lse        : [batch][heads][n] fp32, natural log; may be NULL
  *   scale      : finite, > 0 (1/sqrt(d) is the usual value)
  *   sink_bias  : finite
- *   n >= 1, w >= 1, g >= 0 (g may exceed n), batch >= 1, heads >= 1,
+ *   n >= 1, w >= 1, g >= 0 (g > n is read as g = n: every position is a
+ *   sink either way), batch >= 1, heads >= 1,
  *   n * d * element size < 2^32 (one (batch, head)'s rows are addressed
  *   with 32-bit byte offsets; SWA_EINVAL otherwise).
  * Only the key tiles that hold attended pairs are visited (the diagonal band
@@ -195,7 +196,8 @@ size_t swa_decode_scratch_bytes(void);
  *   k_new, v_new: [batch][kv_heads][t][d]
  *   k_cache, v_cache: [batch][kv_heads][g + w][d]
  *   pos         : [batch] int64, device; a negative entry (or one with
- *                 pos + t beyond INT_MAX) yields NaN rows for that entry
+ *                 pos + t beyond INT_MAX - 1024) yields NaN rows for that
+ *                 entry
  *   lse         : [batch][heads][t] fp32 or NULL
  *   keys        : SWA_KEYS_ALL, or a partial attention over the cache keys
  *                 only (SWA_KEYS_CACHE) or the chunk keys only
@@ -301,7 +303,8 @@ const char *swa_strerror(int status);
  * so masking can be skipped there.  The kernel visits the tiles of its
  * workgroup's query block (bq from swa_prefill_tile_shape) and applies the
  * is_full test to each wave's own 32 query rows.  Returns the number of
- * triples (writing at most `cap`), or a negative status.
+ * triples (writing at most `cap`), or a negative status (SWA_EINVAL also
+ * when n + bq or n + bk exceeds INT_MAX).
  */
 long swa_band_tiles(int n, int w, int g, int bq, int bk, int *out, long cap);
 

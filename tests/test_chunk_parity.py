@@ -198,6 +198,39 @@ def test_chunk_negative_position_gives_nan():
     assert torch.isnan(o[0].float()).all() and torch.isfinite(o[1].float()).all()
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_chunk_far_positions_match_near_ones(dtype):
+    """A chunk at position p0 and at p0 + k w (k w a multiple of the 64-key
+    tile, p0 past w + g) reads the same ring rows and sink rows through the
+    same tiles, so the outputs agree bit for bit; p0 + k w is put at the
+    last accepted position (pos + t = INT_MAX - 1024), where every position
+    sum of the tile arithmetic must still be an int.  One past it gives NaN
+    rows."""
+    dev = _dev()
+    B, H, T, d, w, g, beta = 1, 2, 100, 128, 128, 4, 1.5
+    q = synth.normal((B, H, T, d), seed=11, dtype=dtype, device=dev)
+    kn = synth.normal((B, H, T, d), seed=12, dtype=dtype, device=dev)
+    vn = synth.normal((B, H, T, d), seed=13, dtype=dtype, device=dev)
+    kc = synth.normal((B, H, g + w, d), seed=14, dtype=dtype, device=dev)
+    vc = synth.normal((B, H, g + w, d), seed=15, dtype=dtype, device=dev)
+    last = 2 ** 31 - 1 - 1024 - T             # the largest accepted p0
+    far = last - (last - 1000) % w             # far = near (mod w), near = 1000 + ...
+    near = far % w + 4 * w                     # past w + g, same residue mod w (w is a multiple of 64)
+    assert (far - near) % w == 0 and (far - near) % 64 == 0 and far <= last and near > w + g
+    print(f"chunk at {near} and at {far} (last accepted {last})", flush=True)
+    outs = []
+    for p0 in (near, far):
+        pos = torch.tensor([p0], dtype=torch.int64, device=dev)
+        outs.append(swa.chunk_prefill(q, kn, vn, kc, vc, pos, w=w, g=g, sink_bias=beta, return_lse=True))
+    pos = torch.tensor([last + 1], dtype=torch.int64, device=dev)
+    over = swa.chunk_prefill(q, kn, vn, kc, vc, pos, w=w, g=g, sink_bias=beta)
+    torch.cuda.synchronize()
+    (o_near, l_near), (o_far, l_far) = outs
+    assert torch.isfinite(o_near.float()).all()
+    assert torch.equal(o_near, o_far) and torch.equal(l_near, l_far)
+    assert torch.isnan(over.float()).all()
+
+
 def test_chunk_full_size_sampled(orc):
     """Mistral-shaped chunk: 32 query heads over 8 key/value heads, d=128,
     w=4096, g=4, a 4096-token chunk at position 16384 against a full ring of
