@@ -203,6 +203,26 @@ def test_reference_max_moves_inside_full_tiles(orc, case):
     _compare(orc, q.to(dev), k.to(dev), v.to(dev), w, g, 1.0)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_more_sinks_than_positions_is_g_equal_n(dtype):
+    """g past n (up to INT_MAX) selects every position as a sink, as g = n
+    does: the same output bit for bit, for the plain and the landmark
+    prefill (the tile arithmetic on g stays within int)."""
+    dev = _dev()
+    n = 300
+    q, k, v = synth.qkv(1, 2, n, 128, dtype, seed=31, device=dev)
+    ref, lref = swa.prefill(q, k, v, w=40, g=n, sink_bias=1.5, return_lse=True)
+    for g in (n + 5, 2 ** 31 - 1):
+        print(f"prefill {dtype} n={n} g={g}", flush=True)
+        o, lo = swa.prefill(q, k, v, w=40, g=g, sink_bias=1.5, return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref) and torch.equal(lo, lref), g
+    lm_ref, lm_lref = swa.landmark_prefill(q, k, v, w=40, g=n, r=16, sink_bias=1.5, return_lse=True)
+    lm, lm_l = swa.landmark_prefill(q, k, v, w=40, g=2 ** 31 - 1, r=16, sink_bias=1.5, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(lm, lm_ref) and torch.equal(lm_l, lm_lref)
+
+
 def test_deterministic():
     dev = _dev()
     q, k, v = synth.qkv(1, 4, 3000, 128, torch.bfloat16, seed=21, device=dev)
