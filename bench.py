@@ -105,9 +105,9 @@ MEASURED_TRAFFIC = {
     "chunk_prefill": {"bytes": 117737531, "source_digest": "aafd3b00c1b0755b"},
     "dilated_prefill": {"bytes": 541765770, "source_digest": "aafd3b00c1b0755b"},
     "landmark_prefill": {"bytes": 553675195, "source_digest": "aafd3b00c1b0755b"},
-    "rolling_decode": {"bytes": 4300158266, "source_digest": "b63b9c70bf96ac2b"},
-    "gqa_decode": {"bytes": 1075968367, "source_digest": "b63b9c70bf96ac2b"},
-    "fp8_decode": {"bytes": 2150923135, "source_digest": "b63b9c70bf96ac2b"},
+    "rolling_decode": {"bytes": 4300162623, "source_digest": "255d645b496164ae"},
+    "gqa_decode": {"bytes": 1075969649, "source_digest": "255d645b496164ae"},
+    "fp8_decode": {"bytes": 2150925762, "source_digest": "255d645b496164ae"},
 }
 # Matrix-core figures of the prefill kernels from rocprofv3 counter runs
 # (SQ_INSTS_MFMA, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, SQ_BUSY_CYCLES per

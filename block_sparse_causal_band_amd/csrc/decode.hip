@@ -872,7 +872,9 @@ __global__ __launch_bounds__(256) void kv_append_kernel(uint8_t *__restrict__ kc
     const long long unit = rowid / tn;
     const int b = (int)(unit / heads);
     const int64_t P0 = pos[b];
-    if (P0 < 0) return;
+    // no valid position (a negative one, or one whose last token would pass
+    // INT64_MAX and wrap to a negative ring row): the batch entry is a no-op
+    if (P0 < 0 || P0 > INT64_MAX - tn) return;
     const int64_t P = P0 + j;
     const size_t row_bytes = (size_t)d * ELEM;
     const size_t src = ((size_t)unit * tn + j) * row_bytes + (size_t)chunk * 16;
@@ -947,7 +949,9 @@ __global__ __launch_bounds__(256) void kv_append_fp8_kernel(uint8_t *__restrict_
     const long long unit = rowid / tn;  // batch * heads + head
     const int b = (int)(unit / heads);
     const int64_t P0 = pos[b];
-    if (P0 < 0) return;
+    // no valid position (a negative one, or one whose last token would pass
+    // INT64_MAX and wrap to a negative ring row): the batch entry is a no-op
+    if (P0 < 0 || P0 > INT64_MAX - tn) return;
     const int64_t P = P0 + j;
     const size_t src = ((size_t)unit * tn + j) * d + (size_t)piece * 8;  // element index
     float xk[8], xv[8];

@@ -98,7 +98,8 @@ int swa_prefill_fwd(const void *q, const void *k, const void *v, void *o, float 
  *   k_new, v_new       : [batch][heads][t_new][d]   (dtype)
  *   pos                : [batch] int64, device; position of token 0 of each
  *                        batch entry (token j is at pos[b] + j); must be >= 0
- *                        (a negative entry makes that batch entry a no-op)
+ *                        (a negative entry, or one with pos[b] + t_new past
+ *                        INT64_MAX, makes that batch entry a no-op)
  * A token at position P goes to ring row g + P mod w, and also to sink row P
  * when P < g.  When t_new > w only the last w tokens reach the ring (the
  * earlier ones would be overwritten anyway); sink rows are still written.

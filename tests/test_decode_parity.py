@@ -46,6 +46,42 @@ def test_kv_append_bit_exact(dtype, d, w, g, T, starts):
     assert torch.equal(gk.cpu(), ref_k) and torch.equal(gv.cpu(), ref_v)
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_kv_append_positions_near_int64_max(fp8):
+    """The last accepted start (pos + t_new = INT64_MAX) writes the ring rows
+    the cache model gives for those positions; one further (the last token
+    would wrap past INT64_MAX) leaves the entry untouched, as a negative
+    position does."""
+    dev = _dev()
+    B, H, T, d, w, g = 3, 2, 5, 128, 16, 4
+    top = 2 ** 63 - 1
+    starts = [top - T, top - T + 1, 7]
+    kc0 = synth.normal((B, H, g + w, d), seed=21, dtype=torch.bfloat16)
+    vc0 = synth.normal((B, H, g + w, d), seed=22, dtype=torch.bfloat16)
+    kn = synth.normal((B, H, T, d), seed=23, dtype=torch.bfloat16)
+    vn = synth.normal((B, H, T, d), seed=24, dtype=torch.bfloat16)
+    pos = torch.tensor(starts, dtype=torch.int64)
+    print(f"kv_append{'_fp8' if fp8 else ''} starts {starts}", flush=True)
+    if fp8:
+        scale = torch.full((B, H), 0.05, dtype=torch.float32)
+        codes_k = torch.zeros(B, H, g + w, d, dtype=torch.uint8, device=dev)
+        codes_v = torch.zeros_like(codes_k)
+        swa.kv_append_fp8(codes_k, codes_v, kn.to(dev), vn.to(dev), pos.to(dev), scale.to(dev), scale.to(dev), w=w, g=g)
+        torch.cuda.synchronize()
+        written = (codes_k.cpu() != 0).flatten(2).any(-1)  # [B, H]: rows written per entry
+        assert written[0].all() and not written[1].any() and written[2].all()
+        return
+    expect_k, expect_v = kc0.clone(), vc0.clone()  # entry 1 stays as it was
+    for b in (0, 2):
+        rk, rv = kc0[b:b + 1].clone(), vc0[b:b + 1].clone()
+        cache_model.append(rk, rv, kn[b:b + 1], vn[b:b + 1], [starts[b]], w, g)
+        expect_k[b], expect_v[b] = rk[0], rv[0]
+    gk, gv = kc0.to(dev), vc0.to(dev)
+    swa.kv_append(gk, gv, kn.to(dev), vn.to(dev), pos.to(dev), w=w, g=g)
+    torch.cuda.synchronize()
+    assert torch.equal(gk.cpu(), expect_k) and torch.equal(gv.cpu(), expect_v)
+
+
 def _decode_vs_oracle(orc, q, kc, vc, pos, w, g, beta, units=None, tol=None):
     """GPU decode vs the oracle; the oracle receives logical rows (position,
     k, v) that the cache model says the cache supplies for each query."""
