@@ -710,6 +710,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     using P2 = std::integral_constant<int, 2>;
     using T = std::true_type;
     using F = std::false_type;
+    // Scalar loads still in flight here (kernel arguments the epilogue
+    // needs) would share the LDS counter inside the loop: every tile would
+    // then wait for all its K fragment reads before its first MFMA.
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0) only
     int t = 0;
     for (; t < t_lo; ++t) do_tile_p(t, T{}, P2{}, F{});
     if ((t & 1) && t < t_hi) {
