@@ -98,16 +98,16 @@ PATTERN = {
 # the source has changed since, the figure no longer describes the kernel and
 # `traffic` is reported as null.
 MEASURED_TRAFFIC = {
-    "sink_prefill": {"bytes": 1074172356, "source_digest": "aafd3b00c1b0755b"},
-    "mistral_prefill": {"bytes": 537736873, "source_digest": "aafd3b00c1b0755b"},
-    "gemma3_local_prefill": {"bytes": 2192468673, "source_digest": "aafd3b00c1b0755b"},
-    "gqa_prefill": {"bytes": 336029864, "source_digest": "aafd3b00c1b0755b"},
-    "chunk_prefill": {"bytes": 117737531, "source_digest": "aafd3b00c1b0755b"},
-    "dilated_prefill": {"bytes": 541765770, "source_digest": "aafd3b00c1b0755b"},
-    "landmark_prefill": {"bytes": 553675195, "source_digest": "aafd3b00c1b0755b"},
-    "rolling_decode": {"bytes": 4300162623, "source_digest": "255d645b496164ae"},
-    "gqa_decode": {"bytes": 1075969649, "source_digest": "255d645b496164ae"},
-    "fp8_decode": {"bytes": 2150925762, "source_digest": "255d645b496164ae"},
+    "sink_prefill": {"bytes": 1074000000, "source_digest": "ccfae936886fe8e5"},
+    "mistral_prefill": {"bytes": 537500000, "source_digest": "ccfae936886fe8e5"},
+    "gemma3_local_prefill": {"bytes": 2212000000, "source_digest": "ccfae936886fe8e5"},
+    "gqa_prefill": {"bytes": 336000000, "source_digest": "ccfae936886fe8e5"},
+    "chunk_prefill": {"bytes": 117600000, "source_digest": "ccfae936886fe8e5"},
+    "dilated_prefill": {"bytes": 542000000, "source_digest": "ccfae936886fe8e5"},
+    "landmark_prefill": {"bytes": 553800000, "source_digest": "ccfae936886fe8e5"},
+    "rolling_decode": {"bytes": 4300000000, "source_digest": "255d645b496164ae"},
+    "gqa_decode": {"bytes": 1076000000, "source_digest": "255d645b496164ae"},
+    "fp8_decode": {"bytes": 2151000000, "source_digest": "255d645b496164ae"},
 }
 # Matrix-core figures of the prefill kernels from rocprofv3 counter runs
 # (SQ_INSTS_MFMA, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, SQ_BUSY_CYCLES per
@@ -117,20 +117,20 @@ MEASURED_TRAFFIC = {
 #   mfma_busy_per_simd: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs);
 #   clock_ghz: GRBM_GUI_ACTIVE / 8 XCDs / kernel duration.
 MEASURED_COUNTERS = {
-    "sink_prefill": {"issued_per_band": 1.0448, "mfma_busy_per_simd": 0.5984, "clock_ghz": 1.809,
-                     "valu_per_mfma": 4.78, "source_digest": "aafd3b00c1b0755b"},
-    "mistral_prefill": {"issued_per_band": 1.0312, "mfma_busy_per_simd": 0.5748, "clock_ghz": 1.867,
-                        "valu_per_mfma": 4.72, "source_digest": "aafd3b00c1b0755b"},
-    "gemma3_local_prefill": {"issued_per_band": 1.125, "mfma_busy_per_simd": 0.4951, "clock_ghz": 1.938,
-                             "valu_per_mfma": 5.97, "source_digest": "aafd3b00c1b0755b"},
-    "gqa_prefill": {"issued_per_band": 1.0312, "mfma_busy_per_simd": 0.5904, "clock_ghz": 1.844,
-                    "valu_per_mfma": 4.72, "source_digest": "aafd3b00c1b0755b"},
-    "chunk_prefill": {"issued_per_band": 1.0537, "mfma_busy_per_simd": 0.5658, "clock_ghz": 1.856,
-                      "valu_per_mfma": 4.9, "source_digest": "aafd3b00c1b0755b"},
-    "dilated_prefill": {"issued_per_band": 1.1248, "mfma_busy_per_simd": 0.43, "clock_ghz": 2.118,
-                        "valu_per_mfma": 6.22, "source_digest": "aafd3b00c1b0755b"},
-    "landmark_prefill": {"issued_per_band": 1.0494, "mfma_busy_per_simd": 0.5562, "clock_ghz": 1.89,
-                         "valu_per_mfma": 5.01, "source_digest": "aafd3b00c1b0755b"},
+    "sink_prefill": {"issued_per_band": 1.045, "mfma_busy_per_simd": 0.606, "clock_ghz": 1.82,
+                     "valu_per_mfma": 4.78, "source_digest": "ccfae936886fe8e5"},
+    "mistral_prefill": {"issued_per_band": 1.031, "mfma_busy_per_simd": 0.569, "clock_ghz": 1.88,
+                        "valu_per_mfma": 4.72, "source_digest": "ccfae936886fe8e5"},
+    "gemma3_local_prefill": {"issued_per_band": 1.125, "mfma_busy_per_simd": 0.488, "clock_ghz": 1.96,
+                             "valu_per_mfma": 5.97, "source_digest": "ccfae936886fe8e5"},
+    "gqa_prefill": {"issued_per_band": 1.031, "mfma_busy_per_simd": 0.587, "clock_ghz": 1.85,
+                    "valu_per_mfma": 4.72, "source_digest": "ccfae936886fe8e5"},
+    "chunk_prefill": {"issued_per_band": 1.054, "mfma_busy_per_simd": 0.561, "clock_ghz": 1.87,
+                      "valu_per_mfma": 4.9, "source_digest": "ccfae936886fe8e5"},
+    "dilated_prefill": {"issued_per_band": 1.125, "mfma_busy_per_simd": 0.431, "clock_ghz": 2.06,
+                        "valu_per_mfma": 6.22, "source_digest": "ccfae936886fe8e5"},
+    "landmark_prefill": {"issued_per_band": 1.049, "mfma_busy_per_simd": 0.553, "clock_ghz": 1.91,
+                         "valu_per_mfma": 5.01, "source_digest": "ccfae936886fe8e5"},
 }
 CSRC = os.path.join(ROOT, "block_sparse_causal_band_amd", "csrc")
 
