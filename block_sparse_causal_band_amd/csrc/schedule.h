@@ -62,10 +62,11 @@ constexpr int kXcds = 8;
 // Workgroup id -> (unit = batch*head, query block).  Ids that land on the same
 // XCD (id % 8) get a contiguous run of logical work, so neighbouring query
 // blocks of one head -- which read overlapping K/V windows -- share that XCD's
-// L2.  Within a head the query blocks run from the first to the last, so a
-// block's first key tiles (the low end of its window) are the ones the block
-// before it has just read into that L2, and the tiles no earlier block
-// touched (the diagonal) come last, after the block is under way.  With
+// L2, and each K/V row comes from HBM about once.  Within a head the query
+// blocks run from the first to the last (1-3 % faster than the reverse
+// order).  Blocks start faster than one sweeps its keys, so a key's first
+// reader is the block whose window begins at it: a block's first tiles miss
+// in L2 and the rest of its band hits, read there by the blocks after it.  With
 // grouped-query attention (group query heads per key/value head, consecutive
 // units of one batch entry) the group's query heads take the same query
 // block one after another, so all of them read that block's K/V tiles from
