@@ -64,6 +64,28 @@ def test_prefill_gqa_equals_expanded_heads(dtype, H, Hkv):
     assert torch.equal(a, b) and torch.equal(la, lb)
 
 
+
+def test_prefill_gqa_full_size_sampled(orc):
+    """The grouped-query prefill workload at full size (batch 1, 32 query
+    heads over 8 key/value heads, n=16384, d=128, w=4096, bf16), as timed:
+    sampled rows (the band edges, the tail and 40 random rows) of query heads
+    at the start, middle and end of groups, each against the oracle over its
+    own key/value head."""
+    dev = _dev()
+    B, H, Hkv, n, d, w, g = 1, 32, 8, 16384, 128, 4096, 0
+    q, k, v = synth.qkv(B, H, n, d, torch.bfloat16, seed=9, device=dev, kv_heads=Hkv)
+    o, lse = swa.prefill(q, k, v, w=w, g=g, sink_bias=0.0, return_lse=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    fixed = [0, 1, 63, 64, 127, 128, w - 1, w, w + 127, n - 129, n - 128, n - 1]
+    rows = sorted(set(fixed + rng.choice(n, size=40, replace=False).tolist()))
+    for h in (0, 3, 13, 31):
+        j = oracle.kv_head_of(h, H, Hkv)
+        ro, rl = orc.prefill(q[0, h].cpu(), k[0, j].cpu(), v[0, j].cpu(), w=w, g=g, beta=0.0, rows=rows)
+        gate(o[0, h].float().cpu().numpy()[rows], ro, q.dtype, f"gqa prefill full size, head {h} (kv {j})")
+        gate(lse[0, h].cpu().numpy()[rows], rl, q.dtype, f"gqa prefill lse, head {h}")
+
+
 def _decode_gqa_vs_oracle(orc, q, kc, vc, pos, w, g, beta, units=None):
     B, H, d = q.shape
     Hkv = kc.shape[1]
