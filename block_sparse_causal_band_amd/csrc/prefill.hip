@@ -570,7 +570,6 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
         const uint8_t *vb = vcur + voff;
         constexpr int NC = D / 16;       // MFMAs per 32-key score sub-block
         constexpr int NS = 2 * NC;       // score MFMAs per tile
-        constexpr int EPS = 32 / NS;     // exponentials per score MFMA
         constexpr int NP = 4 * (D / 32); // PV MFMAs per tile
         constexpr int VA = 3;            // V^T fragment read-ahead
         auto kfrag = [&](int j) -> bf16x8 {
@@ -586,8 +585,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
             const s16x4 hi = lds_read_tr16(p0 + 8 * 64);
             return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         };
-        // Every K fragment of tile t+1 is read at the top of the tile (on cut
-        // tiles the mask and the row max of tile t then cover the latency).
+        // Every K fragment of tile t+1 is read at the top of the tile; the
+        // vector phase (on cut tiles also the mask and the row max) covers
+        // the latency.
         bf16x8 kf[NS];
         if constexpr (!LAST) {
 #pragma unroll
@@ -602,20 +602,19 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
             update_max(s_cur, m_run, negm, l_run, oacc, c2, tau);
         }
 
-        // The rest of the tile is two interleaved streams, in a fixed order
-        // (sched_barrier pins it; the compiler would otherwise group like
-        // with like, and long runs of MFMAs with no VALU work between them
-        // leave the matrix core and the VALU taking turns):
-        //  A: the score MFMAs of tile t+1, each followed by the exponentials
-        //     of 32/NS scores of tile t, their bf16 packing and row-sum
-        //     dot2s; the first V^T fragments of B are read during its last
-        //     MFMAs;
-        //  B: the PV MFMAs of tile t (V^T fragments read 3 MFMAs ahead).
-        // The last tile has no next tile: its A stream is the exponentials
-        // alone.  The whole stretch runs at raised wave
-        // priority, so when both waves of a SIMD are ready the one feeding
-        // the matrix core issues first.
-        __builtin_amdgcn_s_setprio(1);
+        // The rest of the tile is two phases, in a fixed order (sched_barrier
+        // pins it):
+        //  1. vector work: the exponentials of tile t, their bf16 packing and
+        //     row-sum dot2s, and on FULL tiles the deferred max check;
+        //  2. matrix work at raised wave priority: the score MFMAs of tile
+        //     t+1 (none on the last tile), then the PV MFMAs of tile t, the
+        //     V^T fragments read 3 MFMAs ahead.
+        // The two waves of a SIMD belong to different workgroups at unrelated
+        // points of their tiles: one wave's vector phase issues beside the
+        // other's matrix phase, and the raised priority lets the wave that
+        // feeds the matrix core issue first when both are ready.  (Spreading
+        // the exponentials over the score MFMAs, or the PV MFMAs over both,
+        // gives each wave a uniform mix and measured 2-5 % slower.)
         f32x16 s_nxt[2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
@@ -637,14 +636,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
             else ls0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls0, false);
         };
 #pragma unroll
-        for (int j = 0; j < NS; ++j) {
-            if (j >= NS - VA) vf[j - (NS - VA)] = vfrag(j - (NS - VA));
-            if constexpr (!LAST)
-                s_nxt[j / NC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j], qf[j % NC], s_nxt[j / NC], 0, 0, 0);
-#pragma unroll
-            for (int q = 0; q < EPS / 2; ++q) prob_pair((EPS / 2) * j + q);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int i = 0; i < 16; ++i) prob_pair(i);
+        __builtin_amdgcn_sched_barrier(0);
         if constexpr (!MASKED) {
             // The reference max moves only if some probability reached 2^8;
             // a lane whose bf16 row sum stays below 2^7 has none, so the
@@ -660,6 +653,14 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
             }
         }
 
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            if (j >= NS - VA) vf[j - (NS - VA)] = vfrag(j - (NS - VA));
+            if constexpr (!LAST)
+                s_nxt[j / NC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j], qf[j % NC], s_nxt[j / NC], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
             // probabilities of keys 16 kc + {4 lh + 0..3, 8 + 4 lh + 0..3}, rounded to bf16
