@@ -561,6 +561,11 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
         uint8_t *const vcur = par ? vbuf1 : vbuf0;
         uint8_t *const vnxt = par ? vbuf0 : vbuf1;
         const int k0 = key_block(t) * kBK;
+        // Wave priority over the tile: 1 while this wave issues its DMAs and
+        // K fragment reads (its loads go out ahead of the other wave's vector
+        // work), 0 over the vector phase, 1 over the score MFMAs and 2 over
+        // the PV MFMAs (the wave nearest its barrier goes first).
+        __builtin_amdgcn_s_setprio(1);
         // only cut tiles can be landmark tiles or precede one
         using ML = std::integral_constant<bool, MASKED>;
         if (t + 2 < ntiles) dma_t(true, t + 2, kcur, ML{});
@@ -593,6 +598,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
 #pragma unroll
             for (int j = 0; j < NS; ++j) kf[j] = kfrag(j);
         }
+        __builtin_amdgcn_s_setprio(0);
 
         if constexpr (MASKED) {
             if (LAND && t < nl)  // the row's last landmark below its window: (qi - w) / r
@@ -611,8 +617,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
         //     V^T fragments read 3 MFMAs ahead.
         // The two waves of a SIMD belong to different workgroups at unrelated
         // points of their tiles: one wave's vector phase issues beside the
-        // other's matrix phase, and the raised priority lets the wave that
-        // feeds the matrix core issue first when both are ready.  (Spreading
+        // other's matrix phase, and the priorities let the wave that feeds
+        // the matrix core issue first when both are ready.  (Spreading
         // the exponentials over the score MFMAs, or the PV MFMAs over both,
         // gives each wave a uniform mix and measured 2-5 % slower.)
         f32x16 s_nxt[2];
@@ -661,6 +667,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
                 s_nxt[j / NC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j], qf[j % NC], s_nxt[j / NC], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_s_setprio(2);
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
             // probabilities of keys 16 kc + {4 lh + 0..3, 8 + 4 lh + 0..3}, rounded to bf16
