@@ -98,13 +98,13 @@ PATTERN = {
 # the source has changed since, the figure no longer describes the kernel and
 # `traffic` is reported as null.
 MEASURED_TRAFFIC = {
-    "sink_prefill": {"bytes": 1074000000, "source_digest": "1865d4313964c0a5"},
-    "mistral_prefill": {"bytes": 537500000, "source_digest": "1865d4313964c0a5"},
-    "gemma3_local_prefill": {"bytes": 2212000000, "source_digest": "1865d4313964c0a5"},
-    "gqa_prefill": {"bytes": 336000000, "source_digest": "1865d4313964c0a5"},
-    "chunk_prefill": {"bytes": 117600000, "source_digest": "1865d4313964c0a5"},
-    "dilated_prefill": {"bytes": 542000000, "source_digest": "1865d4313964c0a5"},
-    "landmark_prefill": {"bytes": 553800000, "source_digest": "1865d4313964c0a5"},
+    "sink_prefill": {"bytes": 1074000000, "source_digest": "e7959d24ca1116de"},
+    "mistral_prefill": {"bytes": 537300000, "source_digest": "e7959d24ca1116de"},
+    "gemma3_local_prefill": {"bytes": 2251000000, "source_digest": "e7959d24ca1116de"},
+    "gqa_prefill": {"bytes": 336000000, "source_digest": "e7959d24ca1116de"},
+    "chunk_prefill": {"bytes": 118300000, "source_digest": "e7959d24ca1116de"},
+    "dilated_prefill": {"bytes": 542200000, "source_digest": "e7959d24ca1116de"},
+    "landmark_prefill": {"bytes": 553700000, "source_digest": "e7959d24ca1116de"},
     "rolling_decode": {"bytes": 4300000000, "source_digest": "1726a2c9d6aab72a"},
     "gqa_decode": {"bytes": 1076000000, "source_digest": "1726a2c9d6aab72a"},
     "fp8_decode": {"bytes": 2151000000, "source_digest": "1726a2c9d6aab72a"},
@@ -117,20 +117,20 @@ MEASURED_TRAFFIC = {
 #   mfma_busy_per_simd: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs);
 #   clock_ghz: GRBM_GUI_ACTIVE / 8 XCDs / kernel duration.
 MEASURED_COUNTERS = {
-    "sink_prefill": {"issued_per_band": 1.045, "mfma_busy_per_simd": 0.606, "clock_ghz": 1.82,
-                     "valu_per_mfma": 4.78, "source_digest": "1865d4313964c0a5"},
-    "mistral_prefill": {"issued_per_band": 1.031, "mfma_busy_per_simd": 0.569, "clock_ghz": 1.88,
-                        "valu_per_mfma": 4.72, "source_digest": "1865d4313964c0a5"},
-    "gemma3_local_prefill": {"issued_per_band": 1.125, "mfma_busy_per_simd": 0.488, "clock_ghz": 1.96,
-                             "valu_per_mfma": 5.97, "source_digest": "1865d4313964c0a5"},
-    "gqa_prefill": {"issued_per_band": 1.031, "mfma_busy_per_simd": 0.587, "clock_ghz": 1.85,
-                    "valu_per_mfma": 4.72, "source_digest": "1865d4313964c0a5"},
-    "chunk_prefill": {"issued_per_band": 1.054, "mfma_busy_per_simd": 0.561, "clock_ghz": 1.87,
-                      "valu_per_mfma": 4.9, "source_digest": "1865d4313964c0a5"},
-    "dilated_prefill": {"issued_per_band": 1.125, "mfma_busy_per_simd": 0.431, "clock_ghz": 2.06,
-                        "valu_per_mfma": 6.22, "source_digest": "1865d4313964c0a5"},
-    "landmark_prefill": {"issued_per_band": 1.049, "mfma_busy_per_simd": 0.553, "clock_ghz": 1.91,
-                         "valu_per_mfma": 5.01, "source_digest": "1865d4313964c0a5"},
+    "sink_prefill": {"issued_per_band": 1.045, "mfma_busy_per_simd": 0.627, "clock_ghz": 1.71,
+                     "valu_per_mfma": 4.77, "source_digest": "e7959d24ca1116de"},
+    "mistral_prefill": {"issued_per_band": 1.031, "mfma_busy_per_simd": 0.602, "clock_ghz": 1.75,
+                        "valu_per_mfma": 4.71, "source_digest": "e7959d24ca1116de"},
+    "gemma3_local_prefill": {"issued_per_band": 1.125, "mfma_busy_per_simd": 0.506, "clock_ghz": 1.85,
+                             "valu_per_mfma": 5.94, "source_digest": "e7959d24ca1116de"},
+    "gqa_prefill": {"issued_per_band": 1.031, "mfma_busy_per_simd": 0.614, "clock_ghz": 1.73,
+                    "valu_per_mfma": 4.71, "source_digest": "e7959d24ca1116de"},
+    "chunk_prefill": {"issued_per_band": 1.054, "mfma_busy_per_simd": 0.585, "clock_ghz": 1.81,
+                      "valu_per_mfma": 4.88, "source_digest": "e7959d24ca1116de"},
+    "dilated_prefill": {"issued_per_band": 1.125, "mfma_busy_per_simd": 0.441, "clock_ghz": 2.04,
+                        "valu_per_mfma": 6.19, "source_digest": "e7959d24ca1116de"},
+    "landmark_prefill": {"issued_per_band": 1.049, "mfma_busy_per_simd": 0.59, "clock_ghz": 1.81,
+                         "valu_per_mfma": 5.0, "source_digest": "e7959d24ca1116de"},
 }
 CSRC = os.path.join(ROOT, "block_sparse_causal_band_amd", "csrc")
 
