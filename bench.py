@@ -669,6 +669,10 @@ def _bench(name, steps, warmup, cold=False):
     return bench_decode(name, steps, warmup)
 
 
+# untimed launches before each extra workload (the headline takes --warmup)
+EXTRA_WARMUP = 40
+
+
 def _brief(r):
     keep = ("value", "unit", "ms_per_step", "dtype", "config", "roofline", "cold_cache")
     return {k: r[k] for k in keep if k in r}
@@ -708,11 +712,14 @@ def main():
     if not args.no_extras and args.workload == HEADLINE:
         # the other workloads first: the headline is timed last, on a chip
         # whose clock has settled under load
+        # (each with at least EXTRA_WARMUP untimed launches: with fewer, the
+        # clock has not settled on the short decode kernels)
+        wu = max(args.warmup, EXTRA_WARMUP)
         for name in ("rolling_decode", "gqa_decode", "fp8_decode", "mistral_prefill", "gemma3_local_prefill",
                      "gqa_prefill", "chunk_prefill", "dilated_prefill", "landmark_prefill"):
-            extra[name] = _brief(_bench(name, args.steps, args.warmup))
+            extra[name] = dict(_brief(_bench(name, args.steps, wu)), warmup=wu)
             torch.cuda.empty_cache()
-        extra["kv_append"] = _brief(bench_kv_append("rolling_decode", args.steps, args.warmup))
+        extra["kv_append"] = dict(_brief(bench_kv_append("rolling_decode", args.steps, wu)), warmup=wu)
         torch.cuda.empty_cache()
     r = _bench(args.workload, args.steps, args.warmup,
                cold=(not args.no_cold and args.workload in PREFILL))
