@@ -50,6 +50,16 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "SWA prefill band-TFLOP/s and decode KV GB/s, % of MI355X peak, 1 GPU"
+# The source pages' own figures, reported beside the measurement as context
+# only: neither is a timing of this operation on named hardware.
+CONTEXT_FROM_PAGES = {
+    "flash_attention_speedup": "a factor of at most 7.6 against attention that writes its intermediates to HBM "
+                               "('@akshay_pachaar: 1) Sparse Attention ...', '2. Flash Attention'; no hardware, "
+                               "sizes or window given)",
+    "mistral_7b_window": "w = 4096 in each of 32 layers, so information can travel about 32 x 4096 = 131072 "
+                         "positions ('Sliding Window and Sparse Attention, from Longformer to CSA2', s2; the decode "
+                         "workloads draw positions up to 131072)",
+}
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (matrix and vector)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
@@ -746,6 +756,7 @@ def main():
         line["cold_cache"] = r["cold_cache"]
     if extra:
         line["extra"] = extra
+    line["context_from_pages"] = CONTEXT_FROM_PAGES
     if not args.no_cpu_baseline:
         if args.workload in PREFILL:
             line["cpu_baseline"] = cpu_baseline_prefill(args.workload)
