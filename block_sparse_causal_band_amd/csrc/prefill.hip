@@ -551,6 +551,12 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     scores(kbuf0, s_cur);
     __syncthreads();  // every wave is done with K(0) before K(2) replaces it
 
+    // Key bounds of this wave's rows: a key after dead_hi, or below dead_lo
+    // and not a sink, is attended by none of them.
+    const int qw0 = q0 + wave * 32;  // this wave's first row
+    const int qw_last = min(qw0 + 31, nq - 1);
+    const int dead_hi = qpos(qw_last), dead_lo = qpos(qw0) - wq + 1;
+
     auto do_tile_p = [&](int t, auto masked_tag, auto par_tag, auto last_tag) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_tag)::value;
         constexpr bool LAST = decltype(last_tag)::value;  // the block's last tile: no next tile to score
@@ -600,12 +606,20 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
         }
         __builtin_amdgcn_s_setprio(0);
 
+        // A cut tile none of whose pairs this wave's rows attend adds nothing
+        // to them: its mask, exponentials and PV MFMAs are skipped (the score
+        // MFMAs of the next tile still run).  Landmark tiles, whose keys are
+        // compact indices, always run.
+        bool dead = false;
+        if constexpr (MASKED && !LAND) dead = (k0 > dead_hi) || (k0 + kBK <= dead_lo && k0 >= g);
         if constexpr (MASKED) {
-            if (LAND && t < nl)  // the row's last landmark below its window: (qi - w) / r
-                mask_landmark_tile(s_cur, (qa >= w) ? (qa - w) / ca.r : -1, k0, lh, lk_lo);
-            else
-                mask_tile<CHUNK || STRIDED>(s_cur, qa, k0, lh, khi, wq, g, bias_raw, klo);
-            update_max(s_cur, m_run, negm, l_run, oacc, c2, tau);
+            if (!dead) {
+                if (LAND && t < nl)  // the row's last landmark below its window: (qi - w) / r
+                    mask_landmark_tile(s_cur, (qa >= w) ? (qa - w) / ca.r : -1, k0, lh, lk_lo);
+                else
+                    mask_tile<CHUNK || STRIDED>(s_cur, qa, k0, lh, khi, wq, g, bias_raw, klo);
+                update_max(s_cur, m_run, negm, l_run, oacc, c2, tau);
+            }
         }
 
         // The rest of the tile is two phases, in a fixed order (sched_barrier
@@ -641,8 +655,13 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
             if (i & 1) ls1 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls1, false);
             else ls0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls0, false);
         };
+        if (dead) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) prob_pair(i);
+            for (int i = 0; i < 16; ++i) pw[i] = 0u;  // unread; left undefined, it costs spills
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) prob_pair(i);
+        }
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (!MASKED) {
             // The reference max moves only if some probability reached 2^8;
@@ -668,6 +687,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
             __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_setprio(2);
+        if (!dead) {
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
             // probabilities of keys 16 kc + {4 lh + 0..3, 8 + 4 lh + 0..3}, rounded to bf16
@@ -681,6 +701,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
                 oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk, oacc[cb], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
+        }
         }
         l_run += ls0 + ls1;
         if constexpr (!LAST) {
@@ -698,7 +719,6 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     // (a wave entirely past n keeps all window tiles unmasked: it stores
     // nothing; landmark tiles always take the cut-tile body, whose DMA knows them)
     int t_lo = 0, t_hi = band.count();
-    const int qw0 = q0 + wave * 32;
     if (qw0 < nq) full_range(band, qpos(qw0), qpos(min(qw0 + 31, nq - 1)), khi, wq, g, kBK, &t_lo, &t_hi, klo);
     t_lo += nl;
     t_hi += nl;
