@@ -542,20 +542,31 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     // computes the scores of tile t+1.  During tile t the DMA fills K(t+2) into
     // the K buffer that K(t) left and V(t+1) into the V buffer that V(t-1)
     // left, so every DMA has a whole tile of time to land.
+    // Key bounds of this wave's rows: a key after dead_hi, or below dead_lo
+    // and not a sink, is attended by none of them.
+    const int qw0 = q0 + wave * 32;  // this wave's first row
+    const int qw_last = min(qw0 + 31, nq - 1);
+    const int dead_hi = qpos(qw_last), dead_lo = qpos(qw0) - wq + 1;
     dma_t(true, 0, kbuf0, std::true_type{});
     dma_t(false, 0, vbuf0, std::true_type{});
     if (ntiles > 1) dma_t(true, 1, kbuf1, std::true_type{});
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     f32x16 s_cur[2];
-    scores(kbuf0, s_cur);
+    {
+        // tile 0's scores are not needed when no row of this wave attends it
+        // (the window's first tile for the last two waves of a block)
+        const int kk = key_block(0) * kBK;
+        if (LAND || !(kk > dead_hi || (kk + kBK <= dead_lo && kk >= g))) {
+            scores(kbuf0, s_cur);
+        } else {
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s_cur[sb][r] = 0.f;
+        }
+    }
     __syncthreads();  // every wave is done with K(0) before K(2) replaces it
-
-    // Key bounds of this wave's rows: a key after dead_hi, or below dead_lo
-    // and not a sink, is attended by none of them.
-    const int qw0 = q0 + wave * 32;  // this wave's first row
-    const int qw_last = min(qw0 + 31, nq - 1);
-    const int dead_hi = qpos(qw_last), dead_lo = qpos(qw0) - wq + 1;
 
     auto do_tile_p = [&](int t, auto masked_tag, auto par_tag, auto last_tag) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_tag)::value;
