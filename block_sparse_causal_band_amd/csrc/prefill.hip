@@ -538,15 +538,16 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
         for (int r = 0; r < 16; ++r) oacc[cb][r] = 0.f;
     float m_run = kNegInf, negm = 0.f, l_run = 0.f;
 
-    // Pipeline: while the softmax of tile t runs on the VALU, the matrix core
-    // computes the scores of tile t+1.  During tile t the DMA fills K(t+2) into
-    // the K buffer that K(t) left and V(t+1) into the V buffer that V(t-1)
-    // left, so every DMA has a whole tile of time to land.
     // Key bounds of this wave's rows: a key after dead_hi, or below dead_lo
     // and not a sink, is attended by none of them.
     const int qw0 = q0 + wave * 32;  // this wave's first row
     const int qw_last = min(qw0 + 31, nq - 1);
     const int dead_hi = qpos(qw_last), dead_lo = qpos(qw0) - wq + 1;
+
+    // Pipeline: tile t forms the probabilities of tile t, the scores of tile
+    // t+1 and the PV product of tile t.  During tile t the DMA fills K(t+2)
+    // into the K buffer that K(t) left and V(t+1) into the V buffer that
+    // V(t-1) left, so every DMA has a whole tile of time to land.
     dma_t(true, 0, kbuf0, std::true_type{});
     dma_t(false, 0, vbuf0, std::true_type{});
     if (ntiles > 1) dma_t(true, 1, kbuf1, std::true_type{});
@@ -700,19 +701,19 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
         __builtin_amdgcn_s_setprio(2);
         if (!dead) {
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-            // probabilities of keys 16 kc + {4 lh + 0..3, 8 + 4 lh + 0..3}, rounded to bf16
-            const bf16x8 pk =
-                __builtin_bit_cast(bf16x8, make_uint4(pw[4 * kc], pw[4 * kc + 1], pw[4 * kc + 2], pw[4 * kc + 3]));
+            for (int kc = 0; kc < 4; ++kc) {
+                // probabilities of keys 16 kc + {4 lh + 0..3, 8 + 4 lh + 0..3}, rounded to bf16
+                const bf16x8 pk =
+                    __builtin_bit_cast(bf16x8, make_uint4(pw[4 * kc], pw[4 * kc + 1], pw[4 * kc + 2], pw[4 * kc + 3]));
 #pragma unroll
-            for (int cb = 0; cb < D / 32; ++cb) {
-                const int j = kc * (D / 32) + cb;
-                const bf16x8 a = vf[j % VA];
-                if (j + VA < NP) vf[j % VA] = vfrag(j + VA);
-                oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk, oacc[cb], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int cb = 0; cb < D / 32; ++cb) {
+                    const int j = kc * (D / 32) + cb;
+                    const bf16x8 a = vf[j % VA];
+                    if (j + VA < NP) vf[j % VA] = vfrag(j + VA);
+                    oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk, oacc[cb], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
-        }
         }
         l_run += ls0 + ls1;
         if constexpr (!LAST) {
