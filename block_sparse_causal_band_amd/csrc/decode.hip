@@ -701,8 +701,8 @@ constexpr int heads_cap() { return std::is_same<CK, CacheFp8>::value ? 4 : 8; }
 
 // Split count: enough workgroups to cover the chip, at least 256 cache rows
 // each.  The VALU kernels aim at 2048 workgroups; the MFMA kernel (two
-// workgroups per CU by LDS) at one round of 512, which measured 7 % faster on
-// 64 x 8 key/value heads than four splits.
+// workgroups per CU by LDS) at one round of 512, which measured 2 % faster on
+// 64 x 8 key/value heads than two splits and 7 % faster than four.
 int decode_splits(int jobs, int rows, int kind) {
     const int target = (kind == 2) ? 512 : 2048;
     if (jobs >= ((kind == 2) ? 512 : 1024)) return 1;
