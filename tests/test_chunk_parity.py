@@ -110,6 +110,33 @@ def test_chunk_gqa_vs_oracle(orc, dtype):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_chunk_random_shapes(orc, dtype):
+    """Seeded random chunks: windows narrower and wider than a key tile and
+    than the chunk, sink counts below, at and above a tile, chunk lengths
+    from one row to several blocks, positions before, at and past the first
+    ring wrap, grouped heads and both head sizes; every row of each chunk
+    against the oracle."""
+    dev = _dev()
+    rng = np.random.default_rng(2024)
+    for case in range(6):
+        w = int(rng.integers(1, 300))
+        g = int(rng.choice([0, 1, 4, 64, 70]))
+        T = int(rng.integers(1, 300))
+        p0s = sorted(int(x) for x in rng.integers(0, 3 * w + 200, size=2))
+        d = int(rng.choice([64, 128]))
+        H, Hkv = [(2, 2), (4, 2), (3, 1)][case % 3]
+        beta = float(rng.uniform(-2.0, 4.0))
+        print(f"case {case}: w={w} g={g} T={T} p0s={p0s} d={d} H={H}/{Hkv} {dtype}", flush=True)
+        q, kseq, vseq, kn, vn, kc, vc, pos = _problem(p0s, T, H, Hkv, d, w, g, dtype, seed=300 + 7 * case)
+        o, lse = swa.chunk_prefill(q.to(dev), kn.to(dev), vn.to(dev), kc, vc, pos, w=w, g=g, sink_bias=beta,
+                                   return_lse=True)
+        torch.cuda.synchronize()
+        ro, rl = _oracle_rows(orc, q, kseq, vseq, p0s, T, w, g, beta)
+        gate(o.float().cpu().numpy(), ro, dtype, f"chunk case {case}")
+        gate(lse.cpu().numpy(), rl, dtype, f"chunk case {case} lse")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_partials_merge_to_full(orc, dtype):
     """Cache-only and chunk-only partials merged by swa_lse_merge equal the
     full chunk result and the oracle; a row with no cache key has o = 0 and
