@@ -735,13 +735,11 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     t_lo += nl;
     t_hi += nl;
     // The last tile runs on its own (no next tile to score) and with the
-    // mask, which leaves a FULL tile's scores as they are.  (The chunk
-    // kernel keeps the discarded score stream on its last tile: a separate
-    // last-tile body does not fit its registers without a spill.)
-    if constexpr (!CHUNK) {
-        if (t_hi > ntiles - 1) t_hi = ntiles - 1;
-        if (t_lo > t_hi) t_lo = t_hi;
-    }
+    // mask, which leaves a FULL tile's scores as they are.  (In the chunk
+    // kernel this costs two spilled registers, reloaded on the cut tiles
+    // before the FULL run; skipping the discarded score stream gains more.)
+    if (t_hi > ntiles - 1) t_hi = ntiles - 1;
+    if (t_lo > t_hi) t_lo = t_hi;
     // The FULL run is unrolled by two so that each tile body names its
     // buffers statically (parity 0 / 1); the cut tiles take the parity at run
     // time (2).
@@ -768,12 +766,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
         do_tile_p(t, F{}, P0{}, F{});
         ++t;
     }
-    if constexpr (CHUNK) {
-        for (; t < ntiles; ++t) do_tile_p(t, T{}, P2{}, F{});
-    } else {
-        for (; t < ntiles - 1; ++t) do_tile_p(t, T{}, P2{}, F{});
-        do_tile_p(ntiles - 1, T{}, P2{}, T{});
-    }
+    for (; t < ntiles - 1; ++t) do_tile_p(t, T{}, P2{}, F{});
+    do_tile_p(ntiles - 1, T{}, P2{}, T{});
 
     // the loop's last barrier has every wave past its LDS reads; each wave
     // stages its rows in its own 32 * 2D bytes of the K buffers
