@@ -108,13 +108,13 @@ PATTERN = {
 # the source has changed since, the figure no longer describes the kernel and
 # `traffic` is reported as null.
 MEASURED_TRAFFIC = {
-    "sink_prefill": {"bytes": 1074000000, "source_digest": "6a51ab228b32c11b"},
-    "mistral_prefill": {"bytes": 537300000, "source_digest": "6a51ab228b32c11b"},
-    "gemma3_local_prefill": {"bytes": 2253000000, "source_digest": "6a51ab228b32c11b"},
-    "gqa_prefill": {"bytes": 336000000, "source_digest": "6a51ab228b32c11b"},
-    "chunk_prefill": {"bytes": 118300000, "source_digest": "6a51ab228b32c11b"},
-    "dilated_prefill": {"bytes": 543000000, "source_digest": "6a51ab228b32c11b"},
-    "landmark_prefill": {"bytes": 553700000, "source_digest": "6a51ab228b32c11b"},
+    "sink_prefill": {"bytes": 1074000000, "source_digest": "f47b6414d6a70bab"},
+    "mistral_prefill": {"bytes": 537300000, "source_digest": "f47b6414d6a70bab"},
+    "gemma3_local_prefill": {"bytes": 2253000000, "source_digest": "f47b6414d6a70bab"},
+    "gqa_prefill": {"bytes": 336000000, "source_digest": "f47b6414d6a70bab"},
+    "chunk_prefill": {"bytes": 122500000, "source_digest": "f47b6414d6a70bab"},
+    "dilated_prefill": {"bytes": 542800000, "source_digest": "f47b6414d6a70bab"},
+    "landmark_prefill": {"bytes": 553600000, "source_digest": "f47b6414d6a70bab"},
     "rolling_decode": {"bytes": 4300000000, "source_digest": "1726a2c9d6aab72a"},
     "gqa_decode": {"bytes": 1076000000, "source_digest": "1726a2c9d6aab72a"},
     "fp8_decode": {"bytes": 2151000000, "source_digest": "1726a2c9d6aab72a"},
@@ -127,20 +127,20 @@ MEASURED_TRAFFIC = {
 #   mfma_busy_per_simd: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs);
 #   clock_ghz: GRBM_GUI_ACTIVE / 8 XCDs / kernel duration.
 MEASURED_COUNTERS = {
-    "sink_prefill": {"issued_per_band": 1.037, "mfma_busy_per_simd": 0.633, "clock_ghz": 1.71,
-                     "valu_per_mfma": 4.71, "source_digest": "6a51ab228b32c11b"},
-    "mistral_prefill": {"issued_per_band": 1.02, "mfma_busy_per_simd": 0.615, "clock_ghz": 1.73,
-                        "valu_per_mfma": 4.67, "source_digest": "6a51ab228b32c11b"},
-    "gemma3_local_prefill": {"issued_per_band": 1.078, "mfma_busy_per_simd": 0.477, "clock_ghz": 1.91,
-                             "valu_per_mfma": 5.84, "source_digest": "6a51ab228b32c11b"},
-    "gqa_prefill": {"issued_per_band": 1.02, "mfma_busy_per_simd": 0.627, "clock_ghz": 1.72,
-                    "valu_per_mfma": 4.67, "source_digest": "6a51ab228b32c11b"},
-    "chunk_prefill": {"issued_per_band": 1.046, "mfma_busy_per_simd": 0.568, "clock_ghz": 1.79,
-                      "valu_per_mfma": 4.83, "source_digest": "6a51ab228b32c11b"},
-    "dilated_prefill": {"issued_per_band": 1.08, "mfma_busy_per_simd": 0.424, "clock_ghz": 2.05,
-                        "valu_per_mfma": 6.08, "source_digest": "6a51ab228b32c11b"},
-    "landmark_prefill": {"issued_per_band": 1.049, "mfma_busy_per_simd": 0.59, "clock_ghz": 1.78,
-                         "valu_per_mfma": 5.0, "source_digest": "6a51ab228b32c11b"},
+    "sink_prefill": {"issued_per_band": 1.037, "mfma_busy_per_simd": 0.648, "clock_ghz": 1.73,
+                     "valu_per_mfma": 4.71, "source_digest": "f47b6414d6a70bab"},
+    "mistral_prefill": {"issued_per_band": 1.02, "mfma_busy_per_simd": 0.616, "clock_ghz": 1.77,
+                        "valu_per_mfma": 4.67, "source_digest": "f47b6414d6a70bab"},
+    "gemma3_local_prefill": {"issued_per_band": 1.078, "mfma_busy_per_simd": 0.484, "clock_ghz": 1.92,
+                             "valu_per_mfma": 5.84, "source_digest": "f47b6414d6a70bab"},
+    "gqa_prefill": {"issued_per_band": 1.02, "mfma_busy_per_simd": 0.631, "clock_ghz": 1.75,
+                    "valu_per_mfma": 4.67, "source_digest": "f47b6414d6a70bab"},
+    "chunk_prefill": {"issued_per_band": 1.038, "mfma_busy_per_simd": 0.57, "clock_ghz": 1.81,
+                      "valu_per_mfma": 4.86, "source_digest": "f47b6414d6a70bab"},
+    "dilated_prefill": {"issued_per_band": 1.08, "mfma_busy_per_simd": 0.428, "clock_ghz": 2.02,
+                        "valu_per_mfma": 6.08, "source_digest": "f47b6414d6a70bab"},
+    "landmark_prefill": {"issued_per_band": 1.049, "mfma_busy_per_simd": 0.592, "clock_ghz": 1.81,
+                         "valu_per_mfma": 5.0, "source_digest": "f47b6414d6a70bab"},
 }
 CSRC = os.path.join(ROOT, "block_sparse_causal_band_amd", "csrc")
 
