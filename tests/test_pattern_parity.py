@@ -53,6 +53,32 @@ def test_dilated_vs_oracle(dtype, d, n, w, r):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_patterns_random_shapes(dtype):
+    """Seeded random dilated and landmark shapes: ragged n, windows below and
+    above a key tile, strides from 1 to past the sequence, sinks, grouped
+    heads and both head sizes; every row against the oracle."""
+    dev = _dev()
+    rng = np.random.default_rng(4242)
+    for case in range(8):
+        kind = "dilated" if case % 2 == 0 else "landmark"
+        n = int(rng.integers(1, 900))
+        w = int(rng.integers(1, 300))
+        r = int(rng.choice([1, 2, 3, 5, 16, 64, 1000]))
+        g = 0 if kind == "dilated" else int(rng.choice([0, 1, 4, 70]))
+        beta = 0.0 if kind == "dilated" else float(rng.uniform(-2.0, 4.0))
+        d = int(rng.choice([64, 128]))
+        H, Hkv = [(2, 2), (4, 2), (3, 1), (2, 1)][case % 4]
+        print(f"case {case}: {kind} n={n} w={w} r={r} g={g} d={d} H={H}/{Hkv} {dtype}", flush=True)
+        q, k, v = synth.qkv(1, H, n, d, dtype, seed=500 + case, device=dev, kv_heads=Hkv)
+        if kind == "dilated":
+            o, lse = swa.dilated_prefill(q, k, v, w=w, r=r, return_lse=True)
+        else:
+            o, lse = swa.landmark_prefill(q, k, v, w=w, g=g, r=r, sink_bias=beta, return_lse=True)
+        torch.cuda.synchronize()
+        _check(q, k, v, o, lse, kind, w, g, r, beta)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_dilation_one_is_plain_prefill(dtype):
     dev = _dev()
     q, k, v = synth.qkv(1, 4, 1000, 128, dtype, seed=92, device=dev)
